@@ -1,0 +1,171 @@
+/*
+ * seqcomp -- token-level KV sequence compressor (CSA / HCA) for AMD MI355X.
+ *
+ * C ABI.  Plain pointers and sizes only; device pointers are HIP device
+ * memory of the current device; `stream` is a hipStream_t passed as void*
+ * (NULL = the default stream).
+ *
+ * What is computed (sources are web pages, cited by title and equation):
+ *  - projection, "序列压缩注意力" eq. attn-seqcomp-csa-proj:
+ *        C^a = H W^{KV_a}, C^b = H W^{KV_b}, Z^a = H W^{Z_a}, Z^b = H W^{Z_b}
+ *    (HCA: C = H W^{KV}, Z = H W^{Z});
+ *  - CSA pooling, eq. attn-seqcomp-csa-softmax and eq. attn-seqcomp-csa-pool:
+ *    entry i takes ONE per-channel softmax over the 2m rows
+ *    [Z^a rows m i .. m(i+1)-1 (+ B^a) ; Z^b rows m(i-1) .. m i - 1 (+ B^b)]
+ *    and sums the matching C^a / C^b rows weighted by it;
+ *  - the entry-0 boundary, eq. attn-seqcomp-overlap-bound: the missing b rows
+ *    have logit -inf and vector 0, so entry 0 is the a-stream alone;
+ *  - HCA pooling, eq. attn-seqcomp-hca: a per-channel softmax over the m'
+ *    rows of block i of Z + B, applied to the same rows of C; no overlap.
+ * A sequence of n tokens gives floor(n/m) entries; a partial tail block is
+ * dropped.  Sequences of a packed batch are independent: every sequence's
+ * entry 0 takes the boundary rule, and no window crosses a sequence.
+ *
+ * Layouts (all row-major, element strides in elements):
+ *  - H        [T x d]        rows = tokens, d contiguous.
+ *  - Wt       [S*c x d]      rows = output channels ("nn.Linear" layout,
+ *                            K contiguous).  CSA (S = 4): rows
+ *                            [0,c) = W^{KV_a}^T, [c,2c) = W^{KV_b}^T,
+ *                            [2c,3c) = W^{Z_a}^T, [3c,4c) = W^{Z_b}^T.
+ *                            HCA (S = 2): [W^{KV}^T ; W^{Z}^T].
+ *  - B^a, B^b [m x c] fp32;  B [m x c] fp32 (HCA).  Row r is added to the
+ *                            logits of row r of a block.
+ *  - pooling streams         [T x ld_in] each, channels [0, c) used.
+ *  - out      [E x c]        E = sum_b floor(L_b / m), entries packed
+ *                            sequence after sequence; row stride c.
+ *  - out_scale [E] fp32      only for SEQCOMP_FP8_E4M3 output: entry i is
+ *                            decode(out[i, :]) * out_scale[i], with
+ *                            out_scale[i] = max_ch |entry_i| / 448 (1 if the
+ *                            entry is all zero).
+ *  - cu_seqlens [batch+1] int64: 0 = cu[0] <= cu[1] <= ... <= cu[batch];
+ *    sequence b is rows [cu[b], cu[b+1]).  Both a host copy (validation,
+ *    launch sizing) and a device copy (read by the kernels) are passed; they
+ *    must hold the same values.
+ *
+ * Dtypes: inputs SEQCOMP_F32 or SEQCOMP_BF16 (all inputs of a call share
+ * one dtype; biases are always fp32); outputs SEQCOMP_F32, SEQCOMP_BF16
+ * (round to nearest even) or SEQCOMP_FP8_E4M3 (OCP E4M3FN, saturating,
+ * round to nearest even, per-entry scale).  Accumulation is fp32.
+ *
+ * Alignment: every device pointer 16-byte aligned; ld_in, ld_y multiples of
+ * 16 bytes; d a multiple of 64; c a multiple of 16.
+ *
+ * Ownership: the caller owns every buffer.  The library never allocates or
+ * frees memory; scratch space comes from the caller's `workspace` (size from
+ * seqcomp_workspace_bytes).  It keeps no state between calls and is safe to
+ * call from several host threads on different streams, given disjoint
+ * outputs and workspaces.
+ *
+ * Errors: every argument is validated on the host before any HIP call; on a
+ * failed validation nothing is launched and no output is written.  A launch
+ * failure returns SEQCOMP_E_HIP.  Calls are asynchronous on `stream`:
+ * faults during execution surface at the caller's next synchronisation.
+ * A call with zero entries returns SEQCOMP_OK and launches nothing.
+ */
+#ifndef SEQCOMP_H
+#define SEQCOMP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum seqcomp_status_code {
+  SEQCOMP_OK = 0,
+  SEQCOMP_E_NULL = 1,        /* a required pointer is NULL                      */
+  SEQCOMP_E_SHAPE = 2,       /* a size is out of range or sizes disagree        */
+  SEQCOMP_E_DTYPE = 3,       /* dtype not supported for that argument           */
+  SEQCOMP_E_ALIGN = 4,       /* pointer or row stride not 16-byte aligned       */
+  SEQCOMP_E_ALIAS = 5,       /* an output overlaps an input or the workspace    */
+  SEQCOMP_E_WORKSPACE = 6,   /* workspace missing or smaller than required      */
+  SEQCOMP_E_UNSUPPORTED = 7, /* well-formed but not supported (m, d, c)         */
+  SEQCOMP_E_HIP = 8,         /* a HIP runtime call or kernel launch failed      */
+  SEQCOMP_E_SEQLENS = 9      /* cu_seqlens not 0-based / not non-decreasing / past T */
+};
+
+enum seqcomp_dtype { SEQCOMP_F32 = 0, SEQCOMP_BF16 = 1, SEQCOMP_FP8_E4M3 = 2 };
+enum seqcomp_mode { SEQCOMP_MODE_CSA = 0, SEQCOMP_MODE_HCA = 1 };
+enum seqcomp_op { SEQCOMP_OP_POOL_CSA = 0, SEQCOMP_OP_POOL_HCA = 1, SEQCOMP_OP_FUSED = 2 };
+
+/* Library version, major*10000 + minor*100 + patch. */
+int seqcomp_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* seqcomp_status_string(int status);
+
+/* Number of entries of a packed batch: sum_b floor((cu[b+1]-cu[b]) / m).
+ * Returns -1 if cu_seqlens_host is NULL, batch < 0, m < 1 or cu is malformed. */
+int64_t seqcomp_num_entries(const int64_t* cu_seqlens_host, int64_t batch, int64_t m);
+
+/* Bytes of device workspace a call needs (0 if none).  `op` selects the
+ * call: SEQCOMP_OP_POOL_CSA / SEQCOMP_OP_POOL_HCA (mode ignored) or
+ * SEQCOMP_OP_FUSED with `mode`.  Returns (size_t)-1 on malformed arguments. */
+size_t seqcomp_workspace_bytes(int op, int mode, int64_t m, int64_t c,
+                               const int64_t* cu_seqlens_host, int64_t batch, int out_dtype);
+
+/*
+ * Projection (eq. attn-seqcomp-csa-proj): Y[T x n_out] = H[T x d] * Wt^T,
+ * i.e. Y[t, j] = sum_k H[t, k] Wt[j, k].  For the compressor, n_out = S*c
+ * and Wt is the stacked weight matrix above, so Y's column slabs are
+ * C^a | C^b | Z^a | Z^b (HCA: C | Z) and can be passed to the pooling calls
+ * with ld_in = ld_y.
+ *   H, Wt: in_dtype (F32 or BF16).  Y: out_dtype (F32 or BF16), row stride ld_y >= n_out.
+ *   Requires d % 64 == 0, n_out % 16 == 0.  bf16 uses the MFMA matrix cores
+ *   with fp32 accumulation.  Y must not overlap H or Wt.
+ */
+int seqcomp_project(const void* H, int64_t T, int64_t d, int in_dtype,
+                    const void* Wt, int64_t n_out,
+                    void* Y, int64_t ld_y, int out_dtype, void* stream);
+
+/*
+ * CSA pooling from materialised streams (eq. attn-seqcomp-csa-softmax,
+ * eq. attn-seqcomp-csa-pool, eq. attn-seqcomp-overlap-bound).
+ *   Ca, Cb, Za, Zb: [T x ld_in] of in_dtype, T = cu[batch]; they may be
+ *   column slices of one seqcomp_project output.  Ba, Bb: [m x c] fp32.
+ *   1 <= m <= 256.  out: [E x c] of out_dtype; out_scale: [E] fp32, required
+ *   iff out_dtype is SEQCOMP_FP8_E4M3 (else ignored, may be NULL).
+ *   workspace: seqcomp_workspace_bytes(SEQCOMP_OP_POOL_CSA, ...) bytes.
+ */
+int seqcomp_pool_csa(const void* Ca, const void* Cb, const void* Za, const void* Zb,
+                     int64_t ld_in, int in_dtype,
+                     const float* Ba, const float* Bb, int64_t m, int64_t c,
+                     const int64_t* cu_seqlens_host, const int64_t* cu_seqlens_dev, int64_t batch,
+                     void* out, int out_dtype, float* out_scale,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * HCA pooling from materialised streams (eq. attn-seqcomp-hca).
+ *   C, Z: [T x ld_in] of in_dtype; B: [m x c] fp32; 1 <= m <= 4096.
+ *   Other arguments as seqcomp_pool_csa.
+ */
+int seqcomp_pool_hca(const void* C, const void* Z, int64_t ld_in, int in_dtype,
+                     const float* B, int64_t m, int64_t c,
+                     const int64_t* cu_seqlens_host, const int64_t* cu_seqlens_dev, int64_t batch,
+                     void* out, int out_dtype, float* out_scale,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Fused compressor: projection, logits + bias + boundary, per-channel
+ * softmax, Hadamard-weighted sum and output encoding in one pass over H;
+ * the projected streams stay on chip ("序列压缩注意力", section on the flash
+ * compressor, describes the single-pass idea).
+ *   mode SEQCOMP_MODE_CSA: m must be 4; Wt is [4c x d]; Ba, Bb [4 x c].
+ *   mode SEQCOMP_MODE_HCA: m must be 128; Wt is [2c x d]; Ba is B [128 x c];
+ *                          Bb must be NULL.
+ *   H: [T x d], T = cu[batch]; d % 64 == 0; c % 16 == 0.
+ *   out, out_scale, workspace as in seqcomp_pool_csa, with
+ *   workspace_bytes >= seqcomp_workspace_bytes(SEQCOMP_OP_FUSED, mode, ...).
+ */
+int seqcomp_compress_fused(int mode, int64_t m, const void* H, int64_t d, int in_dtype,
+                           const void* Wt, int64_t c, const float* Ba, const float* Bb,
+                           const int64_t* cu_seqlens_host, const int64_t* cu_seqlens_dev, int64_t batch,
+                           void* out, int out_dtype, float* out_scale,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SEQCOMP_H */

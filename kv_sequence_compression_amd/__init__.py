@@ -1,0 +1,184 @@
+"""seqcomp: the token-level KV sequence compressor (CSA / HCA) on MI355X.
+
+Python face of the C ABI in ``include/seqcomp.h``.  These wrappers only
+marshal torch tensors into pointers, sizes and the current HIP stream, and
+allocate the outputs and the workspace with torch; every step of the
+computation runs in the HIP kernels of ``libseqcomp.so``.
+
+Functions (each returns torch tensors on the inputs' device):
+
+* ``project(H, Wt, out_dtype)``                         -> Y = H Wt^T
+* ``pool_csa(Ca, Cb, Za, Zb, Ba, Bb, m, cu_seqlens, out_dtype)`` -> (entries, scale|None)
+* ``pool_hca(C, Z, B, m, cu_seqlens, out_dtype)``       -> (entries, scale|None)
+* ``compress_fused(mode, H, Wt, Ba, Bb, m, cu_seqlens, out_dtype)`` -> (entries, scale|None)
+
+``out_dtype`` is one of "f32", "bf16", "fp8" (OCP E4M3FN codes stored as
+uint8 with one fp32 scale per entry).
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import _lib
+
+__all__ = ["SeqcompError", "project", "pool_csa", "pool_hca", "compress_fused", "num_entries",
+           "workspace_bytes", "version", "lib"]
+
+_DT_CODE = {"f32": _lib.F32, "bf16": _lib.BF16, "fp8": _lib.FP8_E4M3}
+_TORCH_IN = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16}
+_TORCH_OUT = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
+
+
+class SeqcompError(RuntimeError):
+    """A seqcomp call returned a non-zero status."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib().seqcomp_status_string(status).decode()
+        super().__init__(f"{where}: {msg} (status {status})")
+
+
+def lib():
+    return _lib.load()
+
+
+def version() -> int:
+    return lib().seqcomp_version()
+
+
+def _check(status: int, where: str):
+    if status != _lib.OK:
+        raise SeqcompError(status, where)
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _in_code(t: torch.Tensor) -> int:
+    if t.dtype not in _TORCH_IN:
+        raise TypeError(f"input dtype {t.dtype} not supported (float32 or bfloat16)")
+    return _TORCH_IN[t.dtype]
+
+
+def _cu_arrays(cu_seqlens, device):
+    """Host int64 array (kept alive by the caller) and its device copy."""
+    if isinstance(cu_seqlens, torch.Tensor):
+        host = cu_seqlens.detach().to("cpu", torch.int64).numpy()
+    else:
+        host = np.asarray(cu_seqlens, dtype=np.int64)
+    host = np.ascontiguousarray(host, dtype=np.int64)
+    dev = torch.from_numpy(host).to(device)
+    return host, dev
+
+
+def _i64p(host: np.ndarray):
+    return host.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+
+def num_entries(cu_seqlens, m: int) -> int:
+    host = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    n = lib().seqcomp_num_entries(_i64p(host), host.size - 1, int(m))
+    if n < 0:
+        raise ValueError("malformed cu_seqlens or m")
+    return int(n)
+
+
+def workspace_bytes(op: int, mode: int, m: int, c: int, cu_seqlens, out_dtype: str) -> int:
+    host = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    n = lib().seqcomp_workspace_bytes(op, mode, int(m), int(c), _i64p(host), host.size - 1, _DT_CODE[out_dtype])
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("malformed workspace query")
+    return int(n)
+
+
+def _alloc_out(E: int, c: int, out_dtype: str, device):
+    out = torch.empty((E, c), dtype=_TORCH_OUT[out_dtype], device=device)
+    scale = torch.empty((E,), dtype=torch.float32, device=device) if out_dtype == "fp8" else None
+    return out, scale
+
+
+def _alloc_ws(nbytes: int, device):
+    return torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=device)
+
+
+def project(H: torch.Tensor, Wt: torch.Tensor, out_dtype: str = "bf16") -> torch.Tensor:
+    """Y[T x n_out] = H[T x d] Wt[n_out x d]^T (eq. attn-seqcomp-csa-proj, all streams at once)."""
+    T, d = H.shape
+    n_out = Wt.shape[0]
+    Y = torch.empty((T, n_out), dtype=_TORCH_OUT[out_dtype], device=H.device)
+    _check(lib().seqcomp_project(_ptr(H), T, d, _in_code(H), _ptr(Wt), n_out, _ptr(Y), n_out,
+                                 _DT_CODE[out_dtype], _stream(H.device)), "seqcomp_project")
+    return Y
+
+
+def _pool_args(x: torch.Tensor):
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("pooling streams must be 2-D with unit channel stride")
+    return x.stride(0)
+
+
+def pool_csa(Ca, Cb, Za, Zb, Ba, Bb, m: int, cu_seqlens=None, out_dtype: str = "bf16"):
+    """CSA pooling of materialised streams; returns (entries [E x c], scale [E] or None)."""
+    ld = _pool_args(Ca)
+    if any(_pool_args(x) != ld for x in (Cb, Za, Zb)):
+        raise ValueError("the four streams must share one row stride")
+    c = Ca.shape[1]
+    dev = Ca.device
+    host, cu_dev = _cu_arrays([0, Ca.shape[0]] if cu_seqlens is None else cu_seqlens, dev)
+    E = num_entries(host, m)
+    out, scale = _alloc_out(E, c, out_dtype, dev)
+    ws_n = workspace_bytes(_lib.OP_POOL_CSA, 0, m, c, host, out_dtype)
+    ws = _alloc_ws(ws_n, dev)
+    _check(lib().seqcomp_pool_csa(_ptr(Ca), _ptr(Cb), _ptr(Za), _ptr(Zb), ld, _in_code(Ca), _ptr(Ba), _ptr(Bb),
+                                  int(m), c, _i64p(host), _ptr(cu_dev), host.size - 1, _ptr(out),
+                                  _DT_CODE[out_dtype], _ptr(scale), _ptr(ws), ws_n, _stream(dev)),
+           "seqcomp_pool_csa")
+    return out, scale
+
+
+def pool_hca(C, Z, B, m: int, cu_seqlens=None, out_dtype: str = "bf16"):
+    """HCA pooling of materialised streams; returns (entries [E x c], scale [E] or None)."""
+    ld = _pool_args(C)
+    if _pool_args(Z) != ld:
+        raise ValueError("C and Z must share one row stride")
+    c = C.shape[1]
+    dev = C.device
+    host, cu_dev = _cu_arrays([0, C.shape[0]] if cu_seqlens is None else cu_seqlens, dev)
+    E = num_entries(host, m)
+    out, scale = _alloc_out(E, c, out_dtype, dev)
+    ws_n = workspace_bytes(_lib.OP_POOL_HCA, 0, m, c, host, out_dtype)
+    ws = _alloc_ws(ws_n, dev)
+    _check(lib().seqcomp_pool_hca(_ptr(C), _ptr(Z), ld, _in_code(C), _ptr(B), int(m), c, _i64p(host),
+                                  _ptr(cu_dev), host.size - 1, _ptr(out), _DT_CODE[out_dtype], _ptr(scale),
+                                  _ptr(ws), ws_n, _stream(dev)), "seqcomp_pool_hca")
+    return out, scale
+
+
+def compress_fused(mode: str, H, Wt, Ba, Bb, m: int, cu_seqlens=None, out_dtype: str = "bf16"):
+    """Fused projection + pooling (mode "csa" with m=4, or "hca" with m=128)."""
+    mcode = {"csa": _lib.MODE_CSA, "hca": _lib.MODE_HCA}[mode]
+    T, d = H.shape
+    S = 4 if mode == "csa" else 2
+    c = Wt.shape[0] // S
+    if Wt.shape != (S * c, d):
+        raise ValueError(f"Wt must be [{S}*c x d]")
+    dev = H.device
+    host, cu_dev = _cu_arrays([0, T] if cu_seqlens is None else cu_seqlens, dev)
+    E = num_entries(host, m)
+    out, scale = _alloc_out(E, c, out_dtype, dev)
+    ws_n = workspace_bytes(_lib.OP_FUSED, mcode, m, c, host, out_dtype)
+    ws = _alloc_ws(ws_n, dev)
+    _check(lib().seqcomp_compress_fused(mcode, int(m), _ptr(H), d, _in_code(H), _ptr(Wt), c, _ptr(Ba),
+                                        _ptr(Bb), _i64p(host), _ptr(cu_dev), host.size - 1, _ptr(out),
+                                        _DT_CODE[out_dtype], _ptr(scale), _ptr(ws), ws_n, _stream(dev)),
+           "seqcomp_compress_fused")
+    return out, scale

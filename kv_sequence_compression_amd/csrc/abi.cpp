@@ -1,0 +1,336 @@
+// C ABI of the seqcomp library: argument validation on the host, then the
+// kernel launches on the caller's stream.  Declarations and the contract of
+// every entry point are in include/seqcomp.h.
+#include "seqcomp.h"
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include "launch.hpp"
+
+using namespace seqcomp;
+
+namespace {
+
+constexpr int kVersion = 10000;   // 1.0.0
+constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int elt_size(int dt) { return dt == SEQCOMP_F32 ? 4 : dt == SEQCOMP_BF16 ? 2 : 1; }
+
+inline bool valid_in_dtype(int dt) { return dt == SEQCOMP_F32 || dt == SEQCOMP_BF16; }
+inline bool valid_out_dtype(int dt) { return dt == SEQCOMP_F32 || dt == SEQCOMP_BF16 || dt == SEQCOMP_FP8_E4M3; }
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Range {
+  uintptr_t lo = 0, hi = 0;   // [lo, hi)
+};
+
+inline Range range_of(const void* p, size_t bytes) {
+  Range r;
+  r.lo = reinterpret_cast<uintptr_t>(p);
+  r.hi = r.lo + bytes;
+  return r;
+}
+
+inline bool overlaps(Range a, Range b) {
+  return a.lo != a.hi && b.lo != b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+// Rows [0, T) of a strided matrix: the last row ends at (T-1)*ld + cols.
+inline size_t strided_bytes(int64_t T, int64_t ld, int64_t cols, int es) {
+  if (T <= 0) return 0;
+  return (size_t)(((T - 1) * ld + cols) * es);
+}
+
+// cu_seqlens: 0-based, non-decreasing, total rows within int32.
+int check_cu(const int64_t* cu, int64_t batch, int64_t* total_rows) {
+  if (batch < 0 || batch > (int64_t(1) << 30)) return SEQCOMP_E_SHAPE;
+  if (!cu) return SEQCOMP_E_NULL;
+  if (cu[0] != 0) return SEQCOMP_E_SEQLENS;
+  for (int64_t b = 0; b < batch; ++b)
+    if (cu[b + 1] < cu[b]) return SEQCOMP_E_SEQLENS;
+  if (cu[batch] > kMaxRows) return SEQCOMP_E_SHAPE;
+  *total_rows = cu[batch];
+  return SEQCOMP_OK;
+}
+
+int64_t entries_of(const int64_t* cu, int64_t batch, int64_t m) {
+  int64_t e = 0;
+  for (int64_t b = 0; b < batch; ++b) e += (cu[b + 1] - cu[b]) / m;
+  return e;
+}
+
+inline int hip_status(hipError_t e) {
+  if (e == hipSuccess) return SEQCOMP_OK;
+  if (e == hipErrorNotSupported) return SEQCOMP_E_UNSUPPORTED;
+  return SEQCOMP_E_HIP;
+}
+
+// Workspace layout: [tile table | CSA halo triples (fused CSA) | fp32 staging (fp8 output)].
+struct WsLayout {
+  size_t tiles_off = 0, halo_off = 0, stage_off = 0, total = 0;
+  int64_t n_tiles = 0;
+};
+
+WsLayout ws_layout(int op, int mode, int64_t m, int64_t c, const int64_t* cu, int64_t batch, int out_dtype) {
+  WsLayout w;
+  int64_t tile_rows;
+  if (op == SEQCOMP_OP_POOL_CSA) tile_rows = pool_csa_tile_rows((int)m);
+  else if (op == SEQCOMP_OP_POOL_HCA) tile_rows = pool_hca_tile_rows((int)m);
+  else tile_rows = kFusedTileRows;
+  w.n_tiles = count_tiles(cu, batch, m, tile_rows);
+  const int64_t E = entries_of(cu, batch, m);
+  size_t off = 0;
+  w.tiles_off = off;
+  off = round_up(off + (size_t)w.n_tiles * sizeof(TileRec), 256);
+  w.halo_off = off;
+  if (op == SEQCOMP_OP_FUSED && mode == SEQCOMP_MODE_CSA) off = round_up(off + (size_t)w.n_tiles * 6 * c * 4, 256);
+  w.stage_off = off;
+  if (out_dtype == SEQCOMP_FP8_E4M3) off = round_up(off + (size_t)E * c * 4, 256);
+  w.total = (E == 0) ? 0 : off;
+  return w;
+}
+
+// Output checks shared by the pooling and fused calls.
+int check_output(int out_dtype, const void* out, const float* out_scale, int64_t E, int64_t c, Range* out_r,
+                 Range* scale_r) {
+  if (!valid_out_dtype(out_dtype)) return SEQCOMP_E_DTYPE;
+  *out_r = Range();
+  *scale_r = Range();
+  if (E == 0) return SEQCOMP_OK;
+  if (!out) return SEQCOMP_E_NULL;
+  if (!aligned16(out)) return SEQCOMP_E_ALIGN;
+  *out_r = range_of(out, (size_t)E * c * elt_size(out_dtype));
+  if (out_dtype == SEQCOMP_FP8_E4M3) {
+    if (!out_scale) return SEQCOMP_E_NULL;
+    if (!aligned16(out_scale)) return SEQCOMP_E_ALIGN;
+    *scale_r = range_of(out_scale, (size_t)E * 4);
+    if (overlaps(*out_r, *scale_r)) return SEQCOMP_E_ALIAS;
+  }
+  return SEQCOMP_OK;
+}
+
+int check_workspace(const void* ws, size_t ws_bytes, size_t need, Range* ws_r) {
+  *ws_r = Range();
+  if (need == 0) return SEQCOMP_OK;
+  if (!ws) return SEQCOMP_E_WORKSPACE;
+  if (ws_bytes < need) return SEQCOMP_E_WORKSPACE;
+  if (!aligned16(ws)) return SEQCOMP_E_ALIGN;
+  *ws_r = range_of(ws, need);
+  return SEQCOMP_OK;
+}
+
+// Any written range (outputs, workspace) overlapping any read range or another written range.
+int check_alias(const Range* written, int nw, const Range* read, int nr) {
+  for (int i = 0; i < nw; ++i) {
+    for (int j = 0; j < nr; ++j)
+      if (overlaps(written[i], read[j])) return SEQCOMP_E_ALIAS;
+    for (int j = i + 1; j < nw; ++j)
+      if (overlaps(written[i], written[j])) return SEQCOMP_E_ALIAS;
+  }
+  return SEQCOMP_OK;
+}
+
+// Pooling (fp32 staging when fp8 output), then the fp8 encoder.
+int run_pool(bool csa, const void* const* streams, int64_t ld_in, int in_dtype, const float* Ba, const float* Bb,
+             int64_t m, int64_t c, const int64_t* cu_dev, int64_t batch, int64_t E, void* out, int out_dtype,
+             float* out_scale, void* ws, const WsLayout& L, hipStream_t st) {
+  char* wsb = static_cast<char*>(ws);
+  TileRec* tiles = reinterpret_cast<TileRec*>(wsb + L.tiles_off);
+  const int op = csa ? SEQCOMP_OP_POOL_CSA : SEQCOMP_OP_POOL_HCA;
+  const int tile_rows = op == SEQCOMP_OP_POOL_CSA ? pool_csa_tile_rows((int)m) : pool_hca_tile_rows((int)m);
+  hipError_t e = launch_plan(cu_dev, (int)batch, (int)m, tile_rows, tiles, (int)L.n_tiles, st);
+  if (e != hipSuccess) return hip_status(e);
+  const bool fp8 = out_dtype == SEQCOMP_FP8_E4M3;
+  void* dst = fp8 ? (void*)(wsb + L.stage_off) : out;
+  const int dst_dt = fp8 ? DT_F32 : out_dtype;
+  if (csa)
+    e = launch_pool_csa(in_dtype, dst_dt, streams[0], streams[1], streams[2], streams[3], ld_in, Ba, Bb, (int)m,
+                        (int)c, tiles, (int)L.n_tiles, dst, st);
+  else
+    e = launch_pool_hca(in_dtype, dst_dt, streams[0], streams[1], ld_in, Ba, (int)m, (int)c, tiles,
+                        (int)L.n_tiles, dst, st);
+  if (e != hipSuccess) return hip_status(e);
+  if (fp8) e = launch_quant_fp8(reinterpret_cast<const float*>(dst), E, (int)c, static_cast<uint8_t*>(out),
+                                out_scale, st);
+  return hip_status(e);
+}
+
+int pool_common(bool csa, const void* const* streams, int n_streams, int64_t ld_in, int in_dtype,
+                const float* Ba, const float* Bb, int64_t m, int64_t c, const int64_t* cu_host,
+                const int64_t* cu_dev, int64_t batch, void* out, int out_dtype, float* out_scale, void* ws,
+                size_t ws_bytes, void* stream) {
+  if (!valid_in_dtype(in_dtype)) return SEQCOMP_E_DTYPE;
+  if (!valid_out_dtype(out_dtype)) return SEQCOMP_E_DTYPE;
+  if (m < 1 || m > (csa ? 256 : 4096)) return SEQCOMP_E_UNSUPPORTED;
+  if (c < 16 || c % 16 != 0 || c > (int64_t(1) << 20)) return SEQCOMP_E_UNSUPPORTED;
+  if (ld_in < c) return SEQCOMP_E_SHAPE;
+  const int es = elt_size(in_dtype);
+  if ((ld_in * es) % 16 != 0) return SEQCOMP_E_ALIGN;
+  int64_t T = 0;
+  int st = check_cu(cu_host, batch, &T);
+  if (st) return st;
+  const int64_t E = entries_of(cu_host, batch, m);
+  Range out_r, scale_r;
+  if ((st = check_output(out_dtype, out, out_scale, E, c, &out_r, &scale_r))) return st;
+  if (E == 0) return SEQCOMP_OK;
+  for (int i = 0; i < n_streams; ++i) {
+    if (!streams[i]) return SEQCOMP_E_NULL;
+    if (!aligned16(streams[i])) return SEQCOMP_E_ALIGN;
+  }
+  if (!Ba || (csa && !Bb) || !cu_dev) return SEQCOMP_E_NULL;
+  if (!aligned16(Ba) || (csa && !aligned16(Bb)) || !aligned16(cu_dev)) return SEQCOMP_E_ALIGN;
+  const int op = csa ? SEQCOMP_OP_POOL_CSA : SEQCOMP_OP_POOL_HCA;
+  const WsLayout L = ws_layout(op, 0, m, c, cu_host, batch, out_dtype);
+  Range ws_r;
+  if ((st = check_workspace(ws, ws_bytes, L.total, &ws_r))) return st;
+  Range reads[7];
+  int nr = 0;
+  for (int i = 0; i < n_streams; ++i) reads[nr++] = range_of(streams[i], strided_bytes(T, ld_in, c, es));
+  reads[nr++] = range_of(Ba, (size_t)m * c * 4);
+  if (csa) reads[nr++] = range_of(Bb, (size_t)m * c * 4);
+  reads[nr++] = range_of(cu_dev, (size_t)(batch + 1) * 8);
+  const Range writes[3] = {out_r, scale_r, ws_r};
+  if ((st = check_alias(writes, 3, reads, nr))) return st;
+  return run_pool(csa, streams, ld_in, in_dtype, Ba, Bb, m, c, cu_dev, batch, E, out, out_dtype, out_scale, ws, L,
+                  static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int seqcomp_version(void) { return kVersion; }
+
+const char* seqcomp_status_string(int status) {
+  switch (status) {
+    case SEQCOMP_OK: return "ok";
+    case SEQCOMP_E_NULL: return "a required pointer is NULL";
+    case SEQCOMP_E_SHAPE: return "a size is out of range or sizes disagree";
+    case SEQCOMP_E_DTYPE: return "dtype not supported for this argument";
+    case SEQCOMP_E_ALIGN: return "pointer or row stride not 16-byte aligned";
+    case SEQCOMP_E_ALIAS: return "an output overlaps an input or the workspace";
+    case SEQCOMP_E_WORKSPACE: return "workspace missing or too small";
+    case SEQCOMP_E_UNSUPPORTED: return "configuration not supported (m, d or c)";
+    case SEQCOMP_E_HIP: return "HIP runtime call or kernel launch failed";
+    case SEQCOMP_E_SEQLENS: return "cu_seqlens must start at 0 and be non-decreasing";
+    default: return "unknown status";
+  }
+}
+
+int64_t seqcomp_num_entries(const int64_t* cu_seqlens_host, int64_t batch, int64_t m) {
+  int64_t T;
+  if (m < 1 || check_cu(cu_seqlens_host, batch, &T) != SEQCOMP_OK) return -1;
+  return entries_of(cu_seqlens_host, batch, m);
+}
+
+size_t seqcomp_workspace_bytes(int op, int mode, int64_t m, int64_t c, const int64_t* cu_seqlens_host,
+                               int64_t batch, int out_dtype) {
+  int64_t T;
+  if (op < SEQCOMP_OP_POOL_CSA || op > SEQCOMP_OP_FUSED) return (size_t)-1;
+  if (op == SEQCOMP_OP_FUSED && mode != SEQCOMP_MODE_CSA && mode != SEQCOMP_MODE_HCA) return (size_t)-1;
+  if (m < 1 || c < 1 || !valid_out_dtype(out_dtype)) return (size_t)-1;
+  if (check_cu(cu_seqlens_host, batch, &T) != SEQCOMP_OK) return (size_t)-1;
+  return ws_layout(op, mode, m, c, cu_seqlens_host, batch, out_dtype).total;
+}
+
+int seqcomp_project(const void* H, int64_t T, int64_t d, int in_dtype, const void* Wt, int64_t n_out, void* Y,
+                    int64_t ld_y, int out_dtype, void* stream) {
+  if (!valid_in_dtype(in_dtype)) return SEQCOMP_E_DTYPE;
+  if (out_dtype != SEQCOMP_F32 && out_dtype != SEQCOMP_BF16) return SEQCOMP_E_DTYPE;
+  if (T < 0 || T > kMaxRows || d < 1 || n_out < 1 || ld_y < n_out) return SEQCOMP_E_SHAPE;
+  if (d % 64 != 0 || n_out % 16 != 0 || d > (int64_t(1) << 24) || n_out > (int64_t(1) << 24))
+    return SEQCOMP_E_UNSUPPORTED;
+  if ((ld_y * elt_size(out_dtype)) % 16 != 0) return SEQCOMP_E_ALIGN;
+  // the kernels address one 256-row tile of H and all of Wt with 32-bit byte offsets
+  if (n_out * d * elt_size(in_dtype) >= (int64_t(1) << 32)) return SEQCOMP_E_UNSUPPORTED;
+  if (T == 0) return SEQCOMP_OK;
+  if (!H || !Wt || !Y) return SEQCOMP_E_NULL;
+  if (!aligned16(H) || !aligned16(Wt) || !aligned16(Y)) return SEQCOMP_E_ALIGN;
+  const int es = elt_size(in_dtype);
+  const Range reads[2] = {range_of(H, (size_t)T * d * es), range_of(Wt, (size_t)n_out * d * es)};
+  const Range writes[1] = {range_of(Y, strided_bytes(T, ld_y, n_out, elt_size(out_dtype)))};
+  int st = check_alias(writes, 1, reads, 2);
+  if (st) return st;
+  return hip_status(launch_project(in_dtype, out_dtype, H, T, (int)d, Wt, (int)n_out, Y, ld_y,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+int seqcomp_pool_csa(const void* Ca, const void* Cb, const void* Za, const void* Zb, int64_t ld_in, int in_dtype,
+                     const float* Ba, const float* Bb, int64_t m, int64_t c, const int64_t* cu_seqlens_host,
+                     const int64_t* cu_seqlens_dev, int64_t batch, void* out, int out_dtype, float* out_scale,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  const void* streams[4] = {Ca, Cb, Za, Zb};
+  return pool_common(true, streams, 4, ld_in, in_dtype, Ba, Bb, m, c, cu_seqlens_host, cu_seqlens_dev, batch, out,
+                     out_dtype, out_scale, workspace, workspace_bytes, stream);
+}
+
+int seqcomp_pool_hca(const void* C, const void* Z, int64_t ld_in, int in_dtype, const float* B, int64_t m, int64_t c,
+                     const int64_t* cu_seqlens_host, const int64_t* cu_seqlens_dev, int64_t batch, void* out,
+                     int out_dtype, float* out_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  const void* streams[2] = {C, Z};
+  return pool_common(false, streams, 2, ld_in, in_dtype, B, nullptr, m, c, cu_seqlens_host, cu_seqlens_dev, batch,
+                     out, out_dtype, out_scale, workspace, workspace_bytes, stream);
+}
+
+int seqcomp_compress_fused(int mode, int64_t m, const void* H, int64_t d, int in_dtype, const void* Wt, int64_t c,
+                           const float* Ba, const float* Bb, const int64_t* cu_seqlens_host,
+                           const int64_t* cu_seqlens_dev, int64_t batch, void* out, int out_dtype,
+                           float* out_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  if (mode != SEQCOMP_MODE_CSA && mode != SEQCOMP_MODE_HCA) return SEQCOMP_E_UNSUPPORTED;
+  const bool csa = mode == SEQCOMP_MODE_CSA;
+  if ((csa && m != 4) || (!csa && m != 128)) return SEQCOMP_E_UNSUPPORTED;
+  if (!valid_in_dtype(in_dtype)) return SEQCOMP_E_DTYPE;
+  if (!valid_out_dtype(out_dtype)) return SEQCOMP_E_DTYPE;
+  if (d < 64 || d % 64 != 0 || d > (int64_t(1) << 24)) return SEQCOMP_E_UNSUPPORTED;
+  if (c < 16 || c % 16 != 0 || c > (int64_t(1) << 20)) return SEQCOMP_E_UNSUPPORTED;
+  if (!csa && Bb) return SEQCOMP_E_SHAPE;
+  // the kernels address all of Wt with 32-bit byte offsets
+  if ((csa ? 4 : 2) * c * d * elt_size(in_dtype) >= (int64_t(1) << 32)) return SEQCOMP_E_UNSUPPORTED;
+  int64_t T = 0;
+  int st = check_cu(cu_seqlens_host, batch, &T);
+  if (st) return st;
+  const int64_t E = entries_of(cu_seqlens_host, batch, m);
+  Range out_r, scale_r;
+  if ((st = check_output(out_dtype, out, out_scale, E, c, &out_r, &scale_r))) return st;
+  if (E == 0) return SEQCOMP_OK;
+  if (!H || !Wt || !Ba || (csa && !Bb) || !cu_seqlens_dev) return SEQCOMP_E_NULL;
+  if (!aligned16(H) || !aligned16(Wt) || !aligned16(Ba) || (csa && !aligned16(Bb)) || !aligned16(cu_seqlens_dev))
+    return SEQCOMP_E_ALIGN;
+  const WsLayout L = ws_layout(SEQCOMP_OP_FUSED, mode, m, c, cu_seqlens_host, batch, out_dtype);
+  Range ws_r;
+  if ((st = check_workspace(workspace, workspace_bytes, L.total, &ws_r))) return st;
+  const int es = elt_size(in_dtype);
+  const int S = csa ? 4 : 2;
+  Range reads[5];
+  int nr = 0;
+  reads[nr++] = range_of(H, (size_t)T * d * es);
+  reads[nr++] = range_of(Wt, (size_t)S * c * d * es);
+  reads[nr++] = range_of(Ba, (size_t)m * c * 4);
+  if (csa) reads[nr++] = range_of(Bb, (size_t)m * c * 4);
+  reads[nr++] = range_of(cu_seqlens_dev, (size_t)(batch + 1) * 8);
+  const Range writes[3] = {out_r, scale_r, ws_r};
+  if ((st = check_alias(writes, 3, reads, nr))) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* wsb = static_cast<char*>(workspace);
+  TileRec* tiles = reinterpret_cast<TileRec*>(wsb + L.tiles_off);
+  float* halo = csa ? reinterpret_cast<float*>(wsb + L.halo_off) : nullptr;
+  const bool fp8 = out_dtype == SEQCOMP_FP8_E4M3;
+  void* dst = fp8 ? (void*)(wsb + L.stage_off) : out;
+  const int dst_dt = fp8 ? DT_F32 : out_dtype;
+  hipError_t e = launch_plan(cu_seqlens_dev, (int)batch, (int)m, kFusedTileRows, tiles, (int)L.n_tiles, s);
+  if (e == hipSuccess)
+    e = launch_fused(mode, in_dtype, dst_dt, H, (int)d, Wt, (int)c, Ba, Bb, tiles, (int)L.n_tiles, dst, halo, s);
+  if (e == hipSuccess && csa) e = launch_csa_fixup(dst_dt, tiles, (int)L.n_tiles, (int)c, halo, dst, s);
+  if (e == hipSuccess && fp8)
+    e = launch_quant_fp8(reinterpret_cast<const float*>(dst), E, (int)c, static_cast<uint8_t*>(out), out_scale, s);
+  return hip_status(e);
+}
+
+}  // extern "C"

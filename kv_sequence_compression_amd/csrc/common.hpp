@@ -1,0 +1,147 @@
+// Device-side helpers shared by the seqcomp kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace seqcomp {
+
+// One tile of rows of ONE sequence.  Tiles never cross sequences; a tile's
+// rows all belong to complete blocks of m rows.
+struct TileRec {
+  int32_t row_start;    // first row (packed-batch row index)
+  int32_t n_rows;       // rows of complete blocks in this tile (multiple of m, > 0)
+  int32_t entry_start;  // packed index of the tile's first entry
+  int32_t flags;        // TILE_FIRST: the tile starts its sequence
+};
+static_assert(sizeof(TileRec) == 16, "tile record is one 16-byte load");
+enum : int32_t { TILE_FIRST = 1 };
+
+enum DType : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+
+// log2(e): exp(x) = 2^(x * log2 e); v_exp_f32 evaluates 2^x.
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h16) { return __uint_as_float(h16 << 16); }
+
+// bfloat16 round-to-nearest-even of a finite float (the compressor produces
+// no NaN or infinity): add half an ulp of the kept part, plus one if the
+// kept part is odd, then truncate.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// OCP E4M3FN encoding of a float: saturate |x| to 448 (the largest finite
+// value, 1.75 * 2^8), round to nearest even.  Below 2^-6 the grid is the
+// subnormal step 2^-9, so the code is rint(|x| * 512) (8 is the smallest
+// normal, whose fields are exponent 1, mantissa 0).  Above, keep 3 of the 23
+// mantissa bits with round-half-even on the fp32 bit pattern and rebias the
+// exponent from 127 to 7.  The sign bit is copied, so -0 encodes as 0x80.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fminf(fabsf(x), 448.0f);
+  uint32_t code;
+  if (a < 0.015625f) {
+    code = (uint32_t)__builtin_rintf(a * 512.0f);
+  } else {
+    uint32_t b = __float_as_uint(a);
+    b += 0x7FFFFu + ((b >> 20) & 1u);
+    code = ((((b >> 23) & 0xFFu) - 120u) << 3) | ((b >> 20) & 7u);
+  }
+  return sign | code;
+}
+
+// Online softmax accumulator of one channel: running max M (in log2 units),
+// running sum S of 2^(l - M) and running weighted sum A of 2^(l - M) * v.
+struct SoftAcc {
+  float M, S, A;
+};
+
+__device__ __forceinline__ void softacc_init(SoftAcc& s) {
+  s.M = -INFINITY;
+  s.S = 0.f;
+  s.A = 0.f;
+}
+
+// Merge two partial accumulators (exact up to rounding: rescale both to the
+// larger maximum).  Either side may be empty (M = -inf, S = A = 0).
+__device__ __forceinline__ SoftAcc softacc_merge(SoftAcc x, SoftAcc y) {
+#pragma clang fp contract(off)
+  const float M = fmaxf(x.M, y.M);
+  if (M == -INFINITY) return x;
+  const float fx = exp2_hw(x.M - M);
+  const float fy = exp2_hw(y.M - M);
+  SoftAcc r;
+  r.M = M;
+  r.S = x.S * fx + y.S * fy;
+  r.A = x.A * fx + y.A * fy;
+  return r;
+}
+
+template <int N>
+struct Vec {
+  float v[N];
+};
+
+// 16-byte vector load / store through the vector memory path.
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// Load 8 consecutive channels of one row as floats.
+template <int DT>
+__device__ __forceinline__ void load8(const void* row_ptr, float (&x)[8]);
+
+template <>
+__device__ __forceinline__ void load8<DT_BF16>(const void* p, float (&x)[8]) {
+  const uint4 u = ld16(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+template <>
+__device__ __forceinline__ void load8<DT_F32>(const void* p, float (&x)[8]) {
+  const uint4 a = ld16(p);
+  const uint4 b = ld16(reinterpret_cast<const char*>(p) + 16);
+  x[0] = __uint_as_float(a.x); x[1] = __uint_as_float(a.y);
+  x[2] = __uint_as_float(a.z); x[3] = __uint_as_float(a.w);
+  x[4] = __uint_as_float(b.x); x[5] = __uint_as_float(b.y);
+  x[6] = __uint_as_float(b.z); x[7] = __uint_as_float(b.w);
+}
+
+// Store 8 consecutive channels (bf16 or fp32).
+template <int DT>
+__device__ __forceinline__ void store8(void* p, const float (&x)[8]);
+
+template <>
+__device__ __forceinline__ void store8<DT_BF16>(void* p, const float (&x)[8]) {
+  st16(p, make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                     pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])));
+}
+
+template <>
+__device__ __forceinline__ void store8<DT_F32>(void* p, const float (&x)[8]) {
+  st16(p, make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])));
+  st16(reinterpret_cast<char*>(p) + 16,
+       make_uint4(__float_as_uint(x[4]), __float_as_uint(x[5]), __float_as_uint(x[6]), __float_as_uint(x[7])));
+}
+
+template <int DT>
+struct DTypeSize;
+template <>
+struct DTypeSize<DT_F32> { static constexpr int value = 4; };
+template <>
+struct DTypeSize<DT_BF16> { static constexpr int value = 2; };
+
+}  // namespace seqcomp

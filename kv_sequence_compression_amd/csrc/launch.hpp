@@ -1,0 +1,53 @@
+// Host-side launchers of the seqcomp kernels.  Arguments are validated by
+// the C ABI layer (abi.cpp) before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace seqcomp {
+
+// Rows per tile of the pooling kernels and of the fused kernels.
+inline int pool_csa_tile_rows(int m) { return m * (m >= 256 ? 1 : 256 / m); }
+inline int pool_hca_tile_rows(int m) { return m * (m >= 512 ? 1 : 512 / m); }
+constexpr int kFusedTileRows = 256;   // MFMA macro-tile height (tokens)
+
+// Host mirror of the device planner: number of tiles of a packed batch.
+int64_t count_tiles(const int64_t* cu, int64_t batch, int64_t m, int64_t tile_rows);
+
+// Writes the tile table of a packed batch (one workgroup).
+hipError_t launch_plan(const int64_t* cu_dev, int batch, int m, int tile_rows,
+                       TileRec* tiles, int n_tiles, hipStream_t stream);
+
+// CSA pooling over tiles; out is [E x c] of out_dt (DT_F32 or DT_BF16).
+hipError_t launch_pool_csa(int in_dt, int out_dt, const void* Ca, const void* Cb, const void* Za,
+                           const void* Zb, int64_t ld_in, const float* Ba, const float* Bb, int m, int c,
+                           const TileRec* tiles, int n_tiles, void* out, hipStream_t stream);
+
+// HCA pooling over tiles; out is [E x c] of out_dt (DT_F32 or DT_BF16).
+hipError_t launch_pool_hca(int in_dt, int out_dt, const void* C, const void* Z, int64_t ld_in,
+                           const float* B, int m, int c, const TileRec* tiles, int n_tiles, void* out,
+                           hipStream_t stream);
+
+// Per-entry scaled OCP E4M3 encoding of fp32 entries [E x c].
+hipError_t launch_quant_fp8(const float* src, int64_t E, int c, uint8_t* out, float* scale,
+                            hipStream_t stream);
+
+// Y[T x n_out] = H[T x d] * Wt[n_out x d]^T.
+hipError_t launch_project(int in_dt, int out_dt, const void* H, int64_t T, int d, const void* Wt,
+                          int n_out, void* Y, int64_t ld_y, hipStream_t stream);
+
+// Fused compressor.  `out` receives DT_F32 or DT_BF16 entries.  For CSA,
+// `halo` holds per tile the fp32 (M, S, A) triples of the first block's
+// a-stream and the last block's b-stream (6 * c floats per tile); the fix-up
+// kernel then writes the first entry of every tile that continues a sequence.
+hipError_t launch_fused(int mode, int in_dt, int out_dt, const void* H, int d, const void* Wt, int c,
+                        const float* Ba, const float* Bb, const TileRec* tiles, int n_tiles, void* out,
+                        float* halo, hipStream_t stream);
+
+hipError_t launch_csa_fixup(int out_dt, const TileRec* tiles, int n_tiles, int c, const float* halo,
+                            void* out, hipStream_t stream);
+
+}  // namespace seqcomp

@@ -1,0 +1,75 @@
+"""Shared test helpers: tolerance checks against the float64 oracle.
+
+Tolerances (written out in every test that uses them):
+* fp32 inputs and fp32 output on the pooling path: max |gpu - oracle| <= 1e-5;
+* bf16 paths (bf16 GEMM operands or bf16 output): per entry row,
+  max_ch |gpu - ref| / max_ch |ref| <= 2e-2;
+* fp8 output: |s_gpu / s_ref - 1| <= 2e-2, and per element
+  |decode(q_gpu) s_gpu - ref| <= ulp_E4M3(|ref| / s_ref) s_ref + base, where
+  `base` is the error bound of the path without fp8 (2e-2 * max_ch |ref_i|
+  for bf16 paths, 1e-5 for fp32 ones): one fp8 step on top of the path error.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+
+
+def to64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def max_abs_err(got: np.ndarray, ref: np.ndarray) -> float:
+    return float(np.max(np.abs(got - ref))) if got.size else 0.0
+
+
+def row_rel_err(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Per-row max |got - ref| / max |ref|."""
+    if got.size == 0:
+        return np.zeros(0)
+    num = np.abs(got - ref).max(axis=1)
+    den = np.maximum(np.abs(ref).max(axis=1), 1e-30)
+    return num / den
+
+
+def e4m3_step(x: np.ndarray) -> np.ndarray:
+    """Spacing of E4M3 values at magnitude x (scaled domain): 2^(floor(log2 x) - 3),
+    2^-9 in the subnormal range."""
+    ax = np.abs(x)
+    e = np.floor(np.log2(np.maximum(ax, 2.0 ** -6)))
+    return np.where(ax < 2.0 ** -6, 2.0 ** -9, 2.0 ** (e - 3))
+
+
+def check_fp8(codes: torch.Tensor, scale: torch.Tensor, ref: np.ndarray, path_rel: float, path_abs: float = 0.0):
+    """Assert the fp8 tolerance; returns (max scale rel err, max excess)."""
+    q = codes.cpu().numpy().astype(np.uint8)
+    s = scale.cpu().double().numpy()
+    amax = np.abs(ref).max(axis=1)
+    s_ref = np.where(amax > 0, amax / oracle.FP8_E4M3_MAX, 1.0)
+    srel = np.abs(s / s_ref - 1.0)
+    assert np.all(srel <= 2e-2), f"scale rel err {srel.max()}"
+    dec = oracle.fp8_e4m3_decode(q) * s[:, None]
+    bound = e4m3_step(ref / s_ref[:, None]) * s_ref[:, None] + path_rel * amax[:, None] + path_abs
+    excess = np.abs(dec - ref) - bound
+    assert np.all(excess <= 0), f"fp8 error exceeds bound by {excess.max()} at {np.unravel_index(np.argmax(excess), excess.shape)}"
+    return float(srel.max()), float(excess.max())
+
+
+def sample_entries(E: int, k: int, seed: int = 0, must=()) -> np.ndarray:
+    """Sorted sample of k entry indices in [0, E) plus the `must` ones (clipped)."""
+    rng = np.random.default_rng(seed)
+    picks = set(int(x) for x in must if 0 <= x < E)
+    if E > 0:
+        picks.update(int(x) for x in rng.choice(E, size=min(k, E), replace=False))
+    return np.array(sorted(picks), dtype=np.int64)
+
+
+def entry_owner(cu: np.ndarray, m: int, idx: np.ndarray):
+    """Map packed entry indices to (sequence, local entry)."""
+    counts = np.diff(cu) // m
+    starts = np.concatenate([[0], np.cumsum(counts)])
+    seq = np.searchsorted(starts, idx, side="right") - 1
+    return seq, idx - starts[seq]

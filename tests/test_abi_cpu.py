@@ -1,0 +1,162 @@
+"""Host-side tests of the C ABI: the library loads, exports every declared
+symbol, and rejects malformed arguments before any HIP call (so these run
+without a GPU; no call here reaches a kernel launch)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from kv_sequence_compression_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "seqcomp.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def _declared():
+    txt = open(HEADER, encoding="utf-8").read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(seqcomp_\w+)\s*\(", txt)))
+
+
+def _status_codes():
+    txt = open(HEADER, encoding="utf-8").read()
+    return {k: int(v) for k, v in re.findall(r"(SEQCOMP_E_\w+|SEQCOMP_OK)\s*=\s*(\d+)", txt)}
+
+
+S = _status_codes()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert set(names) == set(_lib.SIGNATURES), names
+    for nm in names:
+        assert hasattr(lib, nm)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.seqcomp_version() == 10000
+    for code in range(0, 12):
+        assert lib.seqcomp_status_string(code)
+    assert lib.seqcomp_status_string(S["SEQCOMP_E_ALIAS"]).decode().startswith("an output overlaps")
+
+
+def _cu(*vals):
+    return np.ascontiguousarray(np.array(vals, dtype=np.int64))
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+
+def test_num_entries_and_workspace(lib):
+    cu = _cu(0, 64, 100, 100, 107)
+    assert lib.seqcomp_num_entries(_p(cu), 4, 4) == 16 + 9 + 0 + 1
+    assert lib.seqcomp_num_entries(_p(cu), 4, 128) == 0
+    assert lib.seqcomp_num_entries(_p(_cu(1, 5)), 1, 4) == -1
+    assert lib.seqcomp_num_entries(_p(_cu(0, 5, 3)), 2, 4) == -1
+    assert lib.seqcomp_num_entries(_p(cu), 4, 0) == -1
+    # bf16 output: tile table only; fp8 adds fp32 staging; fused CSA adds halo triples
+    one = _cu(0, 8192)
+    tiles = 8192 // 256
+    assert lib.seqcomp_workspace_bytes(_lib.OP_POOL_CSA, 0, 4, 512, _p(one), 1, _lib.BF16) == 512
+    assert lib.seqcomp_workspace_bytes(_lib.OP_POOL_CSA, 0, 4, 512, _p(one), 1, _lib.FP8_E4M3) == 512 + 2048 * 512 * 4
+    assert lib.seqcomp_workspace_bytes(_lib.OP_FUSED, 0, 4, 512, _p(one), 1, _lib.BF16) == 512 + tiles * 6 * 512 * 4
+    assert lib.seqcomp_workspace_bytes(_lib.OP_FUSED, 1, 128, 512, _p(_cu(0, 100)), 1, _lib.BF16) == 0
+    assert lib.seqcomp_workspace_bytes(7, 0, 4, 512, _p(one), 1, _lib.BF16) == ctypes.c_size_t(-1).value
+
+
+# Fake, 16-byte-aligned "device" addresses: validation never dereferences them.
+A, B_, C_, D_ = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+BIAS, BIAS2, CU_DEV, OUT, SCALE, WS = 0x50000000, 0x50100000, 0x50200000, 0x60000000, 0x70000000, 0x80000000
+
+
+def pool_csa(lib, **kw):
+    a = dict(Ca=A, Cb=B_, Za=C_, Zb=D_, ld=512, in_dt=_lib.BF16, Ba=BIAS, Bb=BIAS2, m=4, c=512,
+             cu=_cu(0, 8192), cu_dev=CU_DEV, out=OUT, out_dt=_lib.BF16, scale=0, ws=WS, ws_bytes=1 << 20)
+    a.update(kw)
+    cu = a["cu"]
+    return lib.seqcomp_pool_csa(a["Ca"], a["Cb"], a["Za"], a["Zb"], a["ld"], a["in_dt"], a["Ba"], a["Bb"], a["m"],
+                                a["c"], _p(cu), a["cu_dev"], cu.size - 1, a["out"], a["out_dt"], a["scale"], a["ws"],
+                                a["ws_bytes"], None)
+
+
+def fused(lib, **kw):
+    a = dict(mode=_lib.MODE_CSA, m=4, H=A, d=7168, in_dt=_lib.BF16, Wt=B_, c=512, Ba=BIAS, Bb=BIAS2,
+             cu=_cu(0, 8192), cu_dev=CU_DEV, out=OUT, out_dt=_lib.BF16, scale=0, ws=WS, ws_bytes=1 << 24)
+    a.update(kw)
+    cu = a["cu"]
+    return lib.seqcomp_compress_fused(a["mode"], a["m"], a["H"], a["d"], a["in_dt"], a["Wt"], a["c"], a["Ba"],
+                                      a["Bb"], _p(cu), a["cu_dev"], cu.size - 1, a["out"], a["out_dt"], a["scale"],
+                                      a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(in_dt=7), "SEQCOMP_E_DTYPE"),
+    (dict(in_dt=_lib.FP8_E4M3), "SEQCOMP_E_DTYPE"),
+    (dict(out_dt=9), "SEQCOMP_E_DTYPE"),
+    (dict(Ca=0), "SEQCOMP_E_NULL"),
+    (dict(Bb=0), "SEQCOMP_E_NULL"),
+    (dict(cu_dev=0), "SEQCOMP_E_NULL"),
+    (dict(out=0), "SEQCOMP_E_NULL"),
+    (dict(out_dt=_lib.FP8_E4M3, scale=0), "SEQCOMP_E_NULL"),
+    (dict(Za=C_ + 2), "SEQCOMP_E_ALIGN"),
+    (dict(ld=516), "SEQCOMP_E_ALIGN"),
+    (dict(ld=256), "SEQCOMP_E_SHAPE"),
+    (dict(cu=_cu(1, 8192)), "SEQCOMP_E_SEQLENS"),
+    (dict(cu=_cu(0, 100, 50)), "SEQCOMP_E_SEQLENS"),
+    (dict(m=0), "SEQCOMP_E_UNSUPPORTED"),
+    (dict(m=300), "SEQCOMP_E_UNSUPPORTED"),
+    (dict(c=24, ld=24), "SEQCOMP_E_UNSUPPORTED"),
+    (dict(ws=0), "SEQCOMP_E_WORKSPACE"),
+    (dict(ws_bytes=16), "SEQCOMP_E_WORKSPACE"),
+    (dict(out=A + 4096), "SEQCOMP_E_ALIAS"),
+    (dict(ws=BIAS), "SEQCOMP_E_ALIAS"),
+    (dict(out=WS), "SEQCOMP_E_ALIAS"),
+])
+def test_pool_rejects_bad_arguments(lib, kw, code):
+    assert pool_csa(lib, **kw) == S[code]
+
+
+def test_zero_entries_return_ok_without_buffers(lib):
+    """A batch with no complete block has zero entries: OK, nothing launched,
+    so NULL buffers are accepted."""
+    assert pool_csa(lib, cu=_cu(0, 3), Ca=0, Cb=0, Za=0, Zb=0, out=0, ws=0, ws_bytes=0, cu_dev=0) == S["SEQCOMP_OK"]
+    assert fused(lib, cu=_cu(0, 100), mode=_lib.MODE_HCA, m=128, Bb=0, H=0, out=0, ws=0, ws_bytes=0) == S["SEQCOMP_OK"]
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(mode=3), "SEQCOMP_E_UNSUPPORTED"),
+    (dict(m=8), "SEQCOMP_E_UNSUPPORTED"),
+    (dict(mode=_lib.MODE_HCA, m=4), "SEQCOMP_E_UNSUPPORTED"),
+    (dict(mode=_lib.MODE_HCA, m=128), "SEQCOMP_E_SHAPE"),          # HCA takes no B^b
+    (dict(d=7200), "SEQCOMP_E_UNSUPPORTED"),
+    (dict(c=500), "SEQCOMP_E_UNSUPPORTED"),
+    (dict(H=0), "SEQCOMP_E_NULL"),
+    (dict(Wt=B_ + 8), "SEQCOMP_E_ALIGN"),
+    (dict(ws_bytes=100), "SEQCOMP_E_WORKSPACE"),
+    (dict(out=A), "SEQCOMP_E_ALIAS"),
+    (dict(ws=B_ + 1024), "SEQCOMP_E_ALIAS"),
+    (dict(cu=_cu(0, -4)), "SEQCOMP_E_SEQLENS"),
+    (dict(cu=_cu(0, 1 << 31)), "SEQCOMP_E_SHAPE"),
+])
+def test_fused_rejects_bad_arguments(lib, kw, code):
+    assert fused(lib, **kw) == S[code]
+
+
+def test_project_rejects_bad_arguments(lib):
+    f = lib.seqcomp_project
+    assert f(A, 64, 64, _lib.BF16, B_, 128, OUT, 128, _lib.FP8_E4M3, None) == S["SEQCOMP_E_DTYPE"]
+    assert f(A, 64, 60, _lib.BF16, B_, 128, OUT, 128, _lib.BF16, None) == S["SEQCOMP_E_UNSUPPORTED"]
+    assert f(A, 64, 64, _lib.BF16, B_, 120, OUT, 120, _lib.BF16, None) == S["SEQCOMP_E_UNSUPPORTED"]
+    assert f(A, 64, 64, _lib.BF16, B_, 128, OUT, 100, _lib.BF16, None) == S["SEQCOMP_E_SHAPE"]
+    assert f(0, 64, 64, _lib.BF16, B_, 128, OUT, 128, _lib.BF16, None) == S["SEQCOMP_E_NULL"]
+    assert f(A, 64, 64, _lib.BF16, B_, 128, A + 64, 128, _lib.BF16, None) == S["SEQCOMP_E_ALIAS"]
+    assert f(A, 0, 64, _lib.BF16, B_, 128, 0, 128, _lib.BF16, None) == S["SEQCOMP_OK"]
