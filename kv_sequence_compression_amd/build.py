@@ -8,6 +8,7 @@ csrc/abi.cpp; objects go to kv_sequence_compression_amd/_build/.
 from __future__ import annotations
 
 import concurrent.futures as cf
+import hashlib
 import os
 import shutil
 import subprocess
@@ -40,6 +41,17 @@ def _hipcc() -> str:
 def sources():
     srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
     return srcs + [os.path.join(CSRC, "abi.cpp")]
+
+
+def source_digest() -> str:
+    """SHA-256 over the library sources and the public header (identifies the
+    kernels a stored profile or counter summary was taken on)."""
+    h = hashlib.sha256()
+    for path in sources() + sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hpp")) + [
+            os.path.join(ROOT, "include", "seqcomp.h")]:
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+    return h.hexdigest()
 
 
 def build(verbose: bool = False) -> str:

@@ -122,19 +122,23 @@ class CompressorCase:
 def compressor_case(mode: str, lengths, d: int, c: int, m: int, *, seed: int = 0,
                     in_dtype: str = "bf16", bias_std: float = 0.02, device="cpu",
                     w_device=None, z_outlier_frac: float = 0.0, z_outlier_scale: float = 30.0,
-                    per_sequence_h: bool = False) -> CompressorCase:
+                    per_sequence_h: bool = False, H: torch.Tensor | None = None) -> CompressorCase:
     """Draw H, the stacked weights and the biases for one compressor call.
 
     `z_outlier_frac` of the Z-weight columns (channels) are multiplied by
     `z_outlier_scale`, so those channels' logits are ~N(0, scale^2) on every
-    row (the softmax-stability stress of the batched workload).
+    row (the softmax-stability stress of the batched workload).  An existing
+    `H` (T x d) may be passed to share hidden states between calls.
     """
     assert mode in ("csa", "hca")
     lengths = np.asarray(lengths, dtype=np.int64)
     cu = cu_from_lengths(lengths)
     T = int(cu[-1])
     w_device = device if w_device is None else w_device
-    if per_sequence_h:
+    if H is not None:
+        if tuple(H.shape) != (T, d):
+            raise ValueError("H does not match the lengths and d")
+    elif per_sequence_h:
         H = torch.empty((T, d), dtype=_TORCH_DTYPES[in_dtype], device=device)
         for b in range(lengths.size):
             H[cu[b]:cu[b + 1]] = normal((int(lengths[b]), d), 1.0, (seed, TID["H"], b), device, in_dtype)
