@@ -124,7 +124,7 @@ int seqcomp_project(const void* H, int64_t T, int64_t d, int in_dtype,
  * eq. attn-seqcomp-csa-pool, eq. attn-seqcomp-overlap-bound).
  *   Ca, Cb, Za, Zb: [T x ld_in] of in_dtype, T = cu[batch]; they may be
  *   column slices of one seqcomp_project output.  Ba, Bb: [m x c] fp32.
- *   1 <= m <= 256.  out: [E x c] of out_dtype; out_scale: [E] fp32, required
+ *   1 <= m <= 16.  out: [E x c] of out_dtype; out_scale: [E] fp32, required
  *   iff out_dtype is SEQCOMP_FP8_E4M3 (else ignored, may be NULL).
  *   workspace: seqcomp_workspace_bytes(SEQCOMP_OP_POOL_CSA, ...) bytes.
  */
@@ -137,7 +137,7 @@ int seqcomp_pool_csa(const void* Ca, const void* Cb, const void* Za, const void*
 
 /*
  * HCA pooling from materialised streams (eq. attn-seqcomp-hca).
- *   C, Z: [T x ld_in] of in_dtype; B: [m x c] fp32; 1 <= m <= 4096.
+ *   C, Z: [T x ld_in] of in_dtype; B: [m x c] fp32; 1 <= m <= 256.
  *   Other arguments as seqcomp_pool_csa.
  */
 int seqcomp_pool_hca(const void* C, const void* Z, int64_t ld_in, int in_dtype,

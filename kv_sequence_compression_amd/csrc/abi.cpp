@@ -167,7 +167,7 @@ int pool_common(bool csa, const void* const* streams, int n_streams, int64_t ld_
                 size_t ws_bytes, void* stream) {
   if (!valid_in_dtype(in_dtype)) return SEQCOMP_E_DTYPE;
   if (!valid_out_dtype(out_dtype)) return SEQCOMP_E_DTYPE;
-  if (m < 1 || m > (csa ? 256 : 4096)) return SEQCOMP_E_UNSUPPORTED;
+  if (m < 1 || m > (csa ? kPoolCsaMaxM : kPoolHcaMaxM)) return SEQCOMP_E_UNSUPPORTED;
   if (c < 16 || c % 16 != 0 || c > (int64_t(1) << 20)) return SEQCOMP_E_UNSUPPORTED;
   if (ld_in < c) return SEQCOMP_E_SHAPE;
   const int es = elt_size(in_dtype);
@@ -187,6 +187,8 @@ int pool_common(bool csa, const void* const* streams, int n_streams, int64_t ld_
   if (!aligned16(Ba) || (csa && !aligned16(Bb)) || !aligned16(cu_dev)) return SEQCOMP_E_ALIGN;
   const int op = csa ? SEQCOMP_OP_POOL_CSA : SEQCOMP_OP_POOL_HCA;
   const WsLayout L = ws_layout(op, 0, m, c, cu_host, batch, out_dtype);
+  // one workgroup per (tile, channel slice of 512 / 64 channels) on a 32-bit grid
+  if (L.n_tiles * (csa ? 1 : (c + 63) / 64) >= (int64_t(1) << 31)) return SEQCOMP_E_UNSUPPORTED;
   Range ws_r;
   if ((st = check_workspace(ws, ws_bytes, L.total, &ws_r))) return st;
   Range reads[7];

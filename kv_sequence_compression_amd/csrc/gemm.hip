@@ -88,11 +88,11 @@ struct Frag<DT_BF16> {
   // one K slab = 64 bf16 = two k32 steps; a lane feeds 8 consecutive k.  The
   // eight B fragments of a step stay in registers; A fragments are read one
   // M subtile at a time so the 256 accumulators keep the AGPR file to themselves.
-  static __device__ __forceinline__ void compute(const char* As, const char* Bs, int lane_off, int x,
+  static __device__ __forceinline__ void compute(const char* As, const char* Bs, int lane_off, int x, int lg,
                                                  int wm, int wn, f32x4_t (&acc)[8][8]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int slot = ((h * 4 + ((threadIdx.x & 63) >> 4)) ^ x) * 16;
+      const int slot = ((h * 4 + lg) ^ x) * 16;
       bf16x8_t b[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j)
@@ -113,11 +113,11 @@ struct Frag<DT_F32> {
   // one K slab = 32 fp32 = one k32 step made of eight 16x16x4 MFMAs; lane
   // (row, g = lane/16) feeds k = 8 g + t at step t, the same permutation of
   // k on both operands, so the dot products are unchanged.
-  static __device__ __forceinline__ void compute(const char* As, const char* Bs, int lane_off, int x,
+  static __device__ __forceinline__ void compute(const char* As, const char* Bs, int lane_off, int x, int lg,
                                                  int wm, int wn, f32x4_t (&acc)[8][8]) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int slot = (((((threadIdx.x & 63) >> 4) * 2) + half) ^ x) * 16;
+      const int slot = ((lg * 2 + half) ^ x) * 16;
       f32x4_t a[8], b[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -150,9 +150,8 @@ __device__ __forceinline__ void load_slab(const char* base, const uint32_t (&off
 
 template <int DIN>
 __device__ __forceinline__ void mainloop(const char* a_base, const uint32_t (&a_off)[8], const char* b_base,
-                                         const uint32_t (&b_off)[8], int nk, char* lds, int wm, int wn,
-                                         f32x4_t (&acc)[8][8]) {
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+                                         const uint32_t (&b_off)[8], int nk, char* lds, int w, int lane, int wm,
+                                         int wn, f32x4_t (&acc)[8][8]) {
   const int lane_off = (lane & 15) * kRowBytes;
   const int x = (lane & 7) ^ ((lane >> 3) & 1);
 #pragma unroll
@@ -171,7 +170,7 @@ __device__ __forceinline__ void mainloop(const char* a_base, const uint32_t (&a_
       load_slab(a_base, a_off, (int64_t)(kt + 1) * kRowBytes, nxt, w);
       load_slab(b_base, b_off, (int64_t)(kt + 1) * kRowBytes, nxt + kTileBytes, w);
     }
-    Frag<DIN>::compute(cur, cur + kTileBytes, lane_off, x, wm, wn, acc);
+    Frag<DIN>::compute(cur, cur + kTileBytes, lane_off, x, lane >> 4, wm, wn, acc);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
@@ -238,8 +237,7 @@ __device__ __forceinline__ void store1(char* out, int64_t idx, float v) {
 }
 
 template <int DOUT>
-__device__ void epilogue_project(const Args& a, f32x4_t (&acc)[8][8], int mt, int nt, int wm, int wn) {
-  const int lane = threadIdx.x & 63;
+__device__ void epilogue_project(const Args& a, f32x4_t (&acc)[8][8], int mt, int nt, int lane, int wm, int wn) {
   const int col = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -260,9 +258,8 @@ __device__ void epilogue_project(const Args& a, f32x4_t (&acc)[8][8], int mt, in
 // accumulator [ms][2 s + h] holds rows 128 wm + 16 ms + 4 g + (0..3) of
 // stream s (C^a, C^b, Z^a, Z^b) at channel 64 nt + 32 wn + 16 h + col.
 template <int DOUT>
-__device__ void epilogue_csa(const Args& a, f32x4_t (&acc)[8][8], const TileRec& t, int tile, int nt, int wm,
-                             int wn, char* lds) {
-  const int lane = threadIdx.x & 63;
+__device__ void epilogue_csa(const Args& a, f32x4_t (&acc)[8][8], const TileRec& t, int tile, int nt, int lane,
+                             int wm, int wn, char* lds) {
   const int col = lane & 15, g = lane >> 4;
   const int c = a.c;
   float* xfer = reinterpret_cast<float*>(lds);       // [wn][h][col][3]: wave row 0 -> wave row 1
@@ -341,8 +338,8 @@ __device__ void epilogue_csa(const Args& a, f32x4_t (&acc)[8][8], const TileRec&
 // HCA epilogue (m' = 128): wave row wm is block wm of the tile; accumulator
 // [ms][q] holds C and [ms][4 + q] holds Z at channel 128 nt + 64 wn + 16 q + col.
 template <int DOUT>
-__device__ void epilogue_hca(const Args& a, f32x4_t (&acc)[8][8], const TileRec& t, int nt, int wm, int wn) {
-  const int lane = threadIdx.x & 63;
+__device__ void epilogue_hca(const Args& a, f32x4_t (&acc)[8][8], const TileRec& t, int nt, int lane, int wm,
+                             int wn) {
   const int col = lane & 15, g = lane >> 4;
   const int c = a.c;
   const bool block_ok = (wm + 1) * 128 <= t.n_rows;
@@ -365,11 +362,15 @@ __device__ void epilogue_hca(const Args& a, f32x4_t (&acc)[8][8], const TileRec&
   }
 }
 
+// One logical tile.  The thread index is passed through an empty asm
+// statement so the compiler cannot hoist lane-derived values out of the
+// persistent loop (they would stay live across the K loop and crowd out the
+// accumulators).
 template <int DIN, int MODE, int DOUT>
-__global__ __launch_bounds__(kThreads, 1) void tile_kernel(Args a) {
-  __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int L = xcd_remap(blockIdx.x, a.n_mt * a.n_nt);
+__device__ __forceinline__ void run_tile(const Args& a, int L, char* lds) {
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int w = tid >> 6, lane = tid & 63;
   const int mt = L / a.n_nt, nt = L - mt * a.n_nt;
   const int wm = w >> 1, wn = w & 1;
 
@@ -396,10 +397,25 @@ __global__ __launch_bounds__(kThreads, 1) void tile_kernel(Args a) {
     b_off[i] = (uint32_t)((int64_t)b_row_of<MODE>(r, nt, a.c, a.n_out) * a.lda + kc * 16);
   }
   f32x4_t acc[8][8];
-  mainloop<DIN>(a_base, a_off, a.Wt, b_off, a.nk, lds, wm, wn, acc);
-  if (MODE == MODE_PROJECT) epilogue_project<DOUT>(a, acc, mt, nt, wm, wn);
-  else if (MODE == MODE_CSA) epilogue_csa<DOUT>(a, acc, t, mt, nt, wm, wn, lds);
-  else epilogue_hca<DOUT>(a, acc, t, nt, wm, wn);
+  mainloop<DIN>(a_base, a_off, a.Wt, b_off, a.nk, lds, w, lane, wm, wn, acc);
+  if (MODE == MODE_PROJECT) epilogue_project<DOUT>(a, acc, mt, nt, lane, wm, wn);
+  else if (MODE == MODE_CSA) epilogue_csa<DOUT>(a, acc, t, mt, nt, lane, wm, wn, lds);
+  else epilogue_hca<DOUT>(a, acc, t, nt, lane, wm, wn);
+}
+
+// Persistent grid: one workgroup per CU walks rounds of gridDim.x logical
+// tiles.  In every round each XCD owns one contiguous range of logical tiles
+// (N fastest), so the workgroups that share an M panel of H start it
+// together and advance through K in step: their H slabs hit in the XCD's L2.
+template <int DIN, int MODE, int DOUT>
+__global__ __launch_bounds__(kThreads, 1) void tile_kernel(Args a) {
+  __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
+  const int G = a.n_mt * a.n_nt;
+  const int P = gridDim.x;
+  for (int L = xcd_remap(blockIdx.x, P); L < G; L += P) {
+    run_tile<DIN, MODE, DOUT>(a, L, lds);
+    __syncthreads();   // the epilogue's LDS use ends before the next tile's loads
+  }
 }
 
 // First entry of every tile that continues a sequence: merge the tile's
@@ -425,10 +441,24 @@ __global__ __launch_bounds__(256) void csa_fixup_kernel(const TileRec* __restric
   }
 }
 
+// Compute units of the current device (one workgroup of the tile kernels fits per CU).
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 template <int DIN, int MODE, int DOUT>
 hipError_t launch_tile(const Args& a, hipStream_t stream) {
   const int G = a.n_mt * a.n_nt;
-  hipLaunchKernelGGL((tile_kernel<DIN, MODE, DOUT>), dim3(G), dim3(kThreads), 0, stream, a);
+  const int P = min(G, cu_count());
+  hipLaunchKernelGGL((tile_kernel<DIN, MODE, DOUT>), dim3(P), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

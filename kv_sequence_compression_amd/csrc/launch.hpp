@@ -10,8 +10,12 @@
 namespace seqcomp {
 
 // Rows per tile of the pooling kernels and of the fused kernels.
-inline int pool_csa_tile_rows(int m) { return m * (m >= 256 ? 1 : 256 / m); }
-inline int pool_hca_tile_rows(int m) { return m * (m >= 512 ? 1 : 512 / m); }
+// Rows per tile of the pooling kernels: CSA (m <= 16) takes as many whole
+// blocks as fit in 256 rows; HCA (m <= 256) takes 4 blocks, one per wave.
+inline int pool_csa_tile_rows(int m) { return m * (256 / m); }
+inline int pool_hca_tile_rows(int m) { return 4 * m; }
+constexpr int kPoolCsaMaxM = 16;
+constexpr int kPoolHcaMaxM = 256;
 constexpr int kFusedTileRows = 256;   // MFMA macro-tile height (tokens)
 
 // Host mirror of the device planner: number of tiles of a packed batch.

@@ -1,6 +1,8 @@
 // Pooling-only kernels: the compressor's softmax pooling over streams that
 // are already in HBM (the unfused path).  HBM-bound: every input element is
-// read exactly once, every entry written once.
+// read exactly once and every entry written once, so the design goal is bytes
+// in flight: few registers per lane (high occupancy), 16-byte loads issued
+// back to back, biases served from LDS.
 //
 // CSA ("序列压缩注意力", eq. attn-seqcomp-csa-softmax / -pool / -overlap-bound):
 //   entry i, channel ch:  softmax over the 2m logits
@@ -9,61 +11,120 @@
 //   applied to C^a / C^b of the same rows.
 // HCA (eq. attn-seqcomp-hca): softmax over Z[m i + r] + B[r], r < m, on C.
 //
-// Work split: a workgroup takes one tile (rows of one sequence); a thread
-// takes (entry, 8-channel vector) items and streams the entry's rows with an
-// online max / sum (fp32, base-2 exponent on logits pre-scaled by log2 e).
+// Logits are kept in log2 units (bias pre-scaled by log2 e in LDS, so the
+// logit is one fma) and exponentiated with v_exp_f32; the per-channel online
+// softmax state is (max, sum, weighted sum) in fp32.
 #include "launch.hpp"
 
 namespace seqcomp {
 
 namespace {
 
-constexpr int kPoolThreads = 256;
+typedef __attribute__((address_space(3))) float lds_f32;   // LDS pointer: ds_read, 32-bit address
 
-// Fold up to R rows (row k valid iff k < nvalid) into 8 per-channel online
-// softmax accumulators.  z, v: logit and value rows; bias: B rows (fp32, row
-// stride c floats) for the same rows.
-template <int R>
-__device__ __forceinline__ void fold_rows(SoftAcc (&acc)[8], const float (&z)[R][8], const float (&v)[R][8],
-                                          const float (&bias)[R][8], int nvalid) {
-  // No FMA contraction: the normaliser S and the numerator A take the same
-  // roundings, so value rows of ones give entries of exactly one.
+constexpr int kPoolThreads = 256;
+constexpr int kCsaSlice = 512;    // channels per CSA workgroup
+constexpr int kHcaSlice = 64;     // channels per HCA wave (8 lanes x 8 channels)
+
+// Raw 16-byte row chunk: 8 bf16 or 4 fp32 (an fp32 chunk of 8 channels is two).
+template <int DIN>
+struct Raw8 {
+  uint4 u[DIN == DT_BF16 ? 1 : 2];
+};
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Streamed input: every byte is read exactly once, so the loads are
+// non-temporal (measured on MI355X: ~6.8 TB/s for such reads against
+// ~6.1 TB/s for ordinary loads).
+__device__ __forceinline__ uint4 ld16_stream(const char* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <int DIN>
+__device__ __forceinline__ void ld_raw(Raw8<DIN>& r, const char* p) {
+  r.u[0] = ld16_stream(p);
+  if (DIN == DT_F32) r.u[DIN == DT_F32 ? 1 : 0] = ld16_stream(p + 16);
+}
+
+template <int DIN>
+__device__ __forceinline__ float raw_get(const Raw8<DIN>& r, int j) {
+  if (DIN == DT_BF16) {
+    const uint32_t w = j < 2 ? r.u[0].x : j < 4 ? r.u[0].y : j < 6 ? r.u[0].z : r.u[0].w;
+    return (j & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
+  } else {
+    const uint4& q = r.u[(j >> 2) & (DIN == DT_F32 ? 1 : 0)];
+    const int k = j & 3;
+    return __uint_as_float(k == 0 ? q.x : k == 1 ? q.y : k == 2 ? q.z : q.w);
+  }
+}
+
+// Stage rows [0, m) of a bias slice (channels [ch0, ch0 + width)) into LDS as
+// log2(e) * B, row stride `width`.  All threads of the block take part.
+__device__ __forceinline__ void stage_bias(lds_f32* dst, const float* __restrict__ B, int m, int c, int ch0,
+                                           int width) {
+  for (int i = threadIdx.x; i < m * width; i += blockDim.x) {
+    const int r = i / width, j = i - r * width;
+    const int ch = ch0 + j;
+    dst[i] = ch < c ? B[(int64_t)r * c + ch] * kLog2e : 0.f;
+  }
+}
+
+// Fold 8 rows of 8 channels into the online softmax state with ONE rescale.
+// Row k takes part iff bit k of `valid` is set; the others were loaded from a
+// valid row (finite values) and get logit -inf, hence weight exactly 0, so
+// the code has no branches.  Two passes over the rows (maximum, then
+// exponentials and sums) recompute the logit from the raw 16-byte loads and
+// the LDS bias instead of keeping 64 logits live.
+template <int DIN>
+__device__ __forceinline__ void fold_chunk(SoftAcc (&acc)[8], const Raw8<DIN> (&z)[8], const Raw8<DIN> (&v)[8],
+                                           const lds_f32* const (&bias)[8], uint32_t valid) {
+  // No FMA contraction of the sums: the normaliser S and the numerator A take
+  // the same roundings, so value rows of ones give entries of exactly one.
 #pragma clang fp contract(off)
+  float top[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) top[j] = acc[j].M;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const bool ok = (valid >> k) & 1u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float l = fmaf(raw_get<DIN>(z[k], j), kLog2e, bias[k][j]);
+      top[j] = fmaxf(top[j], ok ? l : -INFINITY);
+    }
+  }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    float l[R];
-    float top = acc[j].M;
+    const float scale = exp2_hw(acc[j].M - top[j]);   // 0 while the state is empty
+    acc[j].S *= scale;
+    acc[j].A *= scale;
+    acc[j].M = top[j];
+  }
 #pragma unroll
-    for (int k = 0; k < R; ++k) {
-      l[k] = k < nvalid ? (z[k][j] + bias[k][j]) * kLog2e : -INFINITY;
-      top = fmaxf(top, l[k]);
-    }
-    if (top == -INFINITY) continue;            // no valid row yet
-    const float scale = exp2_hw(acc[j].M - top);
-    float S = acc[j].S * scale;
-    float A = acc[j].A * scale;
+  for (int k = 0; k < 8; ++k) {
+    const bool ok = (valid >> k) & 1u;
 #pragma unroll
-    for (int k = 0; k < R; ++k) {
-      if (k < nvalid) {                        // rows past nvalid were not loaded
-        const float w = exp2_hw(l[k] - top);
-        S += w;
-        A = fmaf(w, v[k][j], A);
-      }
+    for (int j = 0; j < 8; ++j) {
+      const float l = fmaf(raw_get<DIN>(z[k], j), kLog2e, bias[k][j]);
+      const float w = exp2_hw((ok ? l : -INFINITY) - top[j]);
+      acc[j].S += w;
+      acc[j].A = fmaf(w, raw_get<DIN>(v[k], j), acc[j].A);
     }
-    acc[j].M = top;
-    acc[j].S = S;
-    acc[j].A = A;
   }
 }
 
 template <int DOUT>
-__device__ __forceinline__ void finish_store(const SoftAcc (&acc)[8], char* dst) {
+__device__ __forceinline__ void store_entry8(const SoftAcc (&acc)[8], char* dst) {
   float o[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) o[j] = acc[j].A / acc[j].S;
   store8<DOUT>(dst, o);
 }
 
+// CSA: workgroup = (tile, 512-channel slice); thread item = (entry, 8-channel
+// vector).  Rows are taken four a-rows plus the matching four b-rows at a time.
 template <int DIN, int DOUT>
 __global__ __launch_bounds__(kPoolThreads) void pool_csa_kernel(
     const char* __restrict__ Ca, const char* __restrict__ Cb, const char* __restrict__ Za,
@@ -71,8 +132,17 @@ __global__ __launch_bounds__(kPoolThreads) void pool_csa_kernel(
     int m, int c, const TileRec* __restrict__ tiles, char* __restrict__ out) {
   constexpr int ES = DTypeSize<DIN>::value;
   constexpr int OS = DTypeSize<DOUT>::value;
+  extern __shared__ float sB_[];                // [2][m][width]: log2e * B^a, log2e * B^b
+  lds_f32* sB = (lds_f32*)sB_;
   const TileRec t = tiles[blockIdx.x];
-  const int nv = c >> 3;
+  const int ch0 = blockIdx.y * kCsaSlice;
+  const int width = min(kCsaSlice, c - ch0);
+  lds_f32* sBa = sB;
+  lds_f32* sBb = sB + m * width;
+  stage_bias(sBa, Ba, m, c, ch0, width);
+  stage_bias(sBb, Bb, m, c, ch0, width);
+  __syncthreads();
+  const int nv = width >> 3;
   const int ne = t.n_rows / m;
   const int items = ne * nv;
   for (int it = threadIdx.x; it < items; it += kPoolThreads) {
@@ -80,71 +150,94 @@ __global__ __launch_bounds__(kPoolThreads) void pool_csa_kernel(
     const int v = it - e * nv;
     const int64_t ra = (int64_t)t.row_start + (int64_t)e * m;   // first a-stream row
     const bool has_b = e > 0 || !(t.flags & TILE_FIRST);        // entry 0 of a sequence has no b rows
-    const int64_t col = (int64_t)v * 8 * ES;
+    const int64_t col = (int64_t)(ch0 + v * 8) * ES;
     SoftAcc acc[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) softacc_init(acc[j]);
+#pragma unroll 1
     for (int r0 = 0; r0 < m; r0 += 4) {
       const int na = min(4, m - r0);
-      const int nb = has_b ? na : 0;
-      float za[4][8], ca[4][8], ba[4][8], zb[4][8], cb[4][8], bb[4][8];
+      Raw8<DIN> z[8], x[8];
+      const lds_f32* bias[8];
+      // slots 0..3: a rows r0..r0+3 of block i; slots 4..7: b rows of block
+      // i-1.  Missing rows re-read a valid row and are masked off.
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        if (k < na) {
-          const int64_t row = ra + r0 + k;
-          load8<DIN>(Za + row * ld_bytes + col, za[k]);
-          load8<DIN>(Ca + row * ld_bytes + col, ca[k]);
-          load8<DT_F32>(Ba + (int64_t)(r0 + k) * c + v * 8, ba[k]);
-        }
-        if (k < nb) {
-          const int64_t row = ra - m + r0 + k;
-          load8<DIN>(Zb + row * ld_bytes + col, zb[k]);
-          load8<DIN>(Cb + row * ld_bytes + col, cb[k]);
-          load8<DT_F32>(Bb + (int64_t)(r0 + k) * c + v * 8, bb[k]);
-        }
+        const int r = min(r0 + k, m - 1);
+        const int64_t row_a = ra + r;
+        const int64_t row_b = has_b ? ra - m + r : row_a;
+        ld_raw<DIN>(z[k], Za + row_a * ld_bytes + col);
+        ld_raw<DIN>(x[k], Ca + row_a * ld_bytes + col);
+        ld_raw<DIN>(z[4 + k], Zb + row_b * ld_bytes + col);
+        ld_raw<DIN>(x[4 + k], Cb + row_b * ld_bytes + col);
+        bias[k] = &sBa[r * width + v * 8];
+        bias[4 + k] = &sBb[r * width + v * 8];
       }
-      fold_rows<4>(acc, za, ca, ba, na);
-      fold_rows<4>(acc, zb, cb, bb, nb);
+      const uint32_t amask = (1u << na) - 1u;
+      const uint32_t valid = amask | (has_b ? amask << 4 : 0u);
+      fold_chunk<DIN>(acc, z, x, bias, valid);
     }
-    finish_store<DOUT>(acc, out + ((int64_t)(t.entry_start + e) * c + v * 8) * OS);
+    store_entry8<DOUT>(acc, out + ((int64_t)(t.entry_start + e) * c + ch0 + v * 8) * OS);
   }
 }
 
+// HCA: workgroup = (64-channel slice, tile of 4 entries); wave w takes entry
+// w of the tile.  Lane = 8 g + v: vector v (8 channels) of the slice and row
+// group g, which folds rows g, g + 8, g + 16, ... (so one load instruction
+// reads 8 consecutive rows); three butterfly merges combine the row groups.
 template <int DIN, int DOUT>
 __global__ __launch_bounds__(kPoolThreads) void pool_hca_kernel(
     const char* __restrict__ C, const char* __restrict__ Z, int64_t ld_bytes, const float* __restrict__ B, int m,
     int c, const TileRec* __restrict__ tiles, char* __restrict__ out) {
   constexpr int ES = DTypeSize<DIN>::value;
   constexpr int OS = DTypeSize<DOUT>::value;
-  constexpr int R = 8;
-  const TileRec t = tiles[blockIdx.x];
-  const int nv = c >> 3;
-  const int ne = t.n_rows / m;
-  const int items = ne * nv;
-  for (int it = threadIdx.x; it < items; it += kPoolThreads) {
-    const int e = it / nv;
-    const int v = it - e * nv;
-    const int64_t r_first = (int64_t)t.row_start + (int64_t)e * m;
-    const int64_t col = (int64_t)v * 8 * ES;
-    SoftAcc acc[8];
+  extern __shared__ float sB_[];                  // [m][width]: log2e * B slice
+  lds_f32* sB = (lds_f32*)sB_;
+  // 1-D grid, slice fastest: the slices of one tile are dispatched together
+  const int n_slices = (c + kHcaSlice - 1) / kHcaSlice;
+  const int tile = blockIdx.x / n_slices;
+  const TileRec t = tiles[tile];
+  const int ch0 = (blockIdx.x - tile * n_slices) * kHcaSlice;
+  const int width = min(kHcaSlice, c - ch0);
+  stage_bias(sB, B, m, c, ch0, width);
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int e = threadIdx.x >> 6;
+  const int g = lane >> 3, v = lane & 7;
+  if (e * m >= t.n_rows) return;                  // this tile has fewer entries (no barrier follows)
+  const bool vok = v * 8 < width;
+  const int vv = vok ? v : 0;                     // lanes past the slice re-read vector 0, store nothing
+  const int64_t r_first = (int64_t)t.row_start + (int64_t)e * m;
+  const int64_t col = (int64_t)(ch0 + vv * 8) * ES;
+  SoftAcc acc[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) softacc_init(acc[j]);
-    for (int r0 = 0; r0 < m; r0 += R) {
-      const int nr = min(R, m - r0);
-      float z[R][8], x[R][8], b[R][8];
+  for (int j = 0; j < 8; ++j) softacc_init(acc[j]);
+#pragma unroll 1
+  for (int r0 = g; r0 < m; r0 += 64) {            // this lane's rows r0, r0 + 8, ..., r0 + 56
+    Raw8<DIN> z[8], x[8];
+    const lds_f32* bias[8];
+    uint32_t valid = 0;
 #pragma unroll
-      for (int k = 0; k < R; ++k) {
-        if (k < nr) {
-          const int64_t row = r_first + r0 + k;
-          load8<DIN>(Z + row * ld_bytes + col, z[k]);
-          load8<DIN>(C + row * ld_bytes + col, x[k]);
-          load8<DT_F32>(B + (int64_t)(r0 + k) * c + v * 8, b[k]);
-        }
-      }
-      fold_rows<R>(acc, z, x, b, nr);
+    for (int k = 0; k < 8; ++k) {
+      const int r = r0 + 8 * k;
+      valid |= (r < m ? 1u : 0u) << k;
+      const int rr = min(r, m - 1);               // rows past the block re-read its last row, masked off
+      const int64_t row = r_first + rr;
+      ld_raw<DIN>(z[k], Z + row * ld_bytes + col);
+      ld_raw<DIN>(x[k], C + row * ld_bytes + col);
+      bias[k] = &sB[rr * width + vv * 8];
     }
-    finish_store<DOUT>(acc, out + ((int64_t)(t.entry_start + e) * c + v * 8) * OS);
+    fold_chunk<DIN>(acc, z, x, bias, valid);
   }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    SoftAcc s = acc[j];
+#pragma unroll
+    for (int mask = 8; mask <= 32; mask <<= 1)
+      s = softacc_merge(s, SoftAcc{__shfl_xor(s.M, mask, 64), __shfl_xor(s.S, mask, 64), __shfl_xor(s.A, mask, 64)});
+    acc[j] = s;
+  }
+  if (g == 0 && vok) store_entry8<DOUT>(acc, out + ((int64_t)(t.entry_start + e) * c + ch0 + v * 8) * OS);
 }
 
 }  // namespace
@@ -153,9 +246,10 @@ hipError_t launch_pool_csa(int in_dt, int out_dt, const void* Ca, const void* Cb
                            int64_t ld_in, const float* Ba, const float* Bb, int m, int c, const TileRec* tiles,
                            int n_tiles, void* out, hipStream_t stream) {
   const int64_t ldb = ld_in * (in_dt == DT_BF16 ? 2 : 4);
-  const dim3 grid(n_tiles), block(kPoolThreads);
+  const dim3 grid(n_tiles, (c + kCsaSlice - 1) / kCsaSlice), block(kPoolThreads);
+  const size_t lds = (size_t)2 * m * min(c, kCsaSlice) * sizeof(float);   // <= 64 KiB for m <= 16
   auto args = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, block, 0, stream, (const char*)Ca, (const char*)Cb, (const char*)Za,
+    hipLaunchKernelGGL(kern, grid, block, lds, stream, (const char*)Ca, (const char*)Cb, (const char*)Za,
                        (const char*)Zb, ldb, Ba, Bb, m, c, tiles, (char*)out);
   };
   if (in_dt == DT_BF16 && out_dt == DT_BF16) args(pool_csa_kernel<DT_BF16, DT_BF16>);
@@ -168,9 +262,10 @@ hipError_t launch_pool_csa(int in_dt, int out_dt, const void* Ca, const void* Cb
 hipError_t launch_pool_hca(int in_dt, int out_dt, const void* C, const void* Z, int64_t ld_in, const float* B,
                            int m, int c, const TileRec* tiles, int n_tiles, void* out, hipStream_t stream) {
   const int64_t ldb = ld_in * (in_dt == DT_BF16 ? 2 : 4);
-  const dim3 grid(n_tiles), block(kPoolThreads);
+  const dim3 grid((unsigned)((int64_t)n_tiles * ((c + kHcaSlice - 1) / kHcaSlice))), block(kPoolThreads);
+  const size_t lds = (size_t)m * min(c, kHcaSlice) * sizeof(float);      // <= 64 KiB for m <= 256
   auto args = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, block, 0, stream, (const char*)C, (const char*)Z, ldb, B, m, c, tiles,
+    hipLaunchKernelGGL(kern, grid, block, lds, stream, (const char*)C, (const char*)Z, ldb, B, m, c, tiles,
                        (char*)out);
   };
   if (in_dt == DT_BF16 && out_dt == DT_BF16) args(pool_hca_kernel<DT_BF16, DT_BF16>);

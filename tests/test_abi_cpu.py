@@ -67,6 +67,7 @@ def test_num_entries_and_workspace(lib):
     one = _cu(0, 8192)
     tiles = 8192 // 256
     assert lib.seqcomp_workspace_bytes(_lib.OP_POOL_CSA, 0, 4, 512, _p(one), 1, _lib.BF16) == 512
+    assert lib.seqcomp_workspace_bytes(_lib.OP_POOL_HCA, 0, 128, 512, _p(one), 1, _lib.BF16) == 256   # 16 tiles of 4 entries
     assert lib.seqcomp_workspace_bytes(_lib.OP_POOL_CSA, 0, 4, 512, _p(one), 1, _lib.FP8_E4M3) == 512 + 2048 * 512 * 4
     assert lib.seqcomp_workspace_bytes(_lib.OP_FUSED, 0, 4, 512, _p(one), 1, _lib.BF16) == 512 + tiles * 6 * 512 * 4
     assert lib.seqcomp_workspace_bytes(_lib.OP_FUSED, 1, 128, 512, _p(_cu(0, 100)), 1, _lib.BF16) == 0
@@ -113,7 +114,7 @@ def fused(lib, **kw):
     (dict(cu=_cu(1, 8192)), "SEQCOMP_E_SEQLENS"),
     (dict(cu=_cu(0, 100, 50)), "SEQCOMP_E_SEQLENS"),
     (dict(m=0), "SEQCOMP_E_UNSUPPORTED"),
-    (dict(m=300), "SEQCOMP_E_UNSUPPORTED"),
+    (dict(m=17), "SEQCOMP_E_UNSUPPORTED"),
     (dict(c=24, ld=24), "SEQCOMP_E_UNSUPPORTED"),
     (dict(ws=0), "SEQCOMP_E_WORKSPACE"),
     (dict(ws_bytes=16), "SEQCOMP_E_WORKSPACE"),
