@@ -250,7 +250,8 @@ int seqcomp_project(const void* H, int64_t T, int64_t d, int in_dtype, const voi
     return SEQCOMP_E_UNSUPPORTED;
   if ((ld_y * elt_size(out_dtype)) % 16 != 0) return SEQCOMP_E_ALIGN;
   // the kernels address one 256-row tile of H and all of Wt with 32-bit byte offsets
-  if (n_out * d * elt_size(in_dtype) >= (int64_t(1) << 32)) return SEQCOMP_E_UNSUPPORTED;
+  if (n_out * d * elt_size(in_dtype) >= (int64_t(1) << 32) || 256 * d * elt_size(in_dtype) >= (int64_t(1) << 32))
+    return SEQCOMP_E_UNSUPPORTED;
   if (T == 0) return SEQCOMP_OK;
   if (!H || !Wt || !Y) return SEQCOMP_E_NULL;
   if (!aligned16(H) || !aligned16(Wt) || !aligned16(Y)) return SEQCOMP_E_ALIGN;
@@ -292,8 +293,10 @@ int seqcomp_compress_fused(int mode, int64_t m, const void* H, int64_t d, int in
   if (d < 64 || d % 64 != 0 || d > (int64_t(1) << 24)) return SEQCOMP_E_UNSUPPORTED;
   if (c < 16 || c % 16 != 0 || c > (int64_t(1) << 20)) return SEQCOMP_E_UNSUPPORTED;
   if (!csa && Bb) return SEQCOMP_E_SHAPE;
-  // the kernels address all of Wt with 32-bit byte offsets
-  if ((csa ? 4 : 2) * c * d * elt_size(in_dtype) >= (int64_t(1) << 32)) return SEQCOMP_E_UNSUPPORTED;
+  // the kernels address one 256-row tile of H and all of Wt with 32-bit byte offsets
+  if ((csa ? 4 : 2) * c * d * elt_size(in_dtype) >= (int64_t(1) << 32) ||
+      256 * d * elt_size(in_dtype) >= (int64_t(1) << 32))
+    return SEQCOMP_E_UNSUPPORTED;
   int64_t T = 0;
   int st = check_cu(cu_seqlens_host, batch, &T);
   if (st) return st;

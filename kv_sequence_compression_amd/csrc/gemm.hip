@@ -6,8 +6,12 @@
 // 4 x 4 v_mfma_f32_32x32x16_bf16 accumulators in registers: with one wave per
 // SIMD that instruction sustains ~94% of the bf16 peak on gfx950, the 16x16x32
 // form only ~56%, as measured with back-to-back independent MFMAs).  K advances in
-// 128-byte slabs (64 bf16 / 32 fp32) that are copied global -> LDS directly
-// (global_load_lds_dwordx4, no register staging) into a 2-stage ring.
+// 128-byte slabs (64 bf16 / 32 fp32 of every tile row: whole cache lines, so
+// every L2 request is a full line) that are copied global -> LDS directly
+// (global_load_lds_dwordx4, no register staging).  The LDS holds a ring of
+// 3 slabs of H and 2 of Wt (5 x 32 KiB = 160 KiB): H, streamed from HBM,
+// is requested two slabs ahead, the weights, which hit in L2 or the
+// last-level cache, one slab ahead.
 //
 // The fused kernels keep that accumulator tile in registers and pool it
 // there, so C and Z never reach HBM:
@@ -42,22 +46,24 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kThreads = 256;
 constexpr int kTile = 256;                      // BM = BN = 256
-constexpr int kRowBytes = 64;                   // bytes of one tile row per K slab (32 bf16 / 16 fp32)
-constexpr int kTileBytes = kTile * kRowBytes;   // 16 KiB per operand per stage
-constexpr int kStages = 5;                      // ring depth: 4 slabs of loads in flight
-constexpr int kStageBytes = 2 * kTileBytes;     // A and B
-constexpr int kLdsBytes = kStages * kStageBytes;  // 160 KiB: all of a CU's LDS
+constexpr int kRowBytes = 128;                  // bytes of one tile row per K slab (64 bf16 / 32 fp32)
+constexpr int kSlabBytes = kTile * kRowBytes;   // 32 KiB: one operand's slab
+constexpr int kStagesA = 3;                     // H slabs in the ring
+constexpr int kStagesB = 2;                     // Wt slabs in the ring
+constexpr int kLdsB = kStagesA * kSlabBytes;    // offset of the Wt slots
+constexpr int kLdsBytes = (kStagesA + kStagesB) * kSlabBytes;   // 160 KiB: all of a CU's LDS
+constexpr int kLoadsPerSlab = kTile / 4 / 8;    // global_load_lds per wave and operand slab (8 rows each)
 
 enum : int { MODE_PROJECT = 0, MODE_CSA = 1, MODE_HCA = 2 };
 
-// 16-byte slot of k-chunk kc (0..3) in 64-byte tile row r.  With g(r) =
-// ((r >> 1) ^ (r >> 2)) & 3 the 16 lanes reading one k-chunk of 16
-// consecutive rows hit distinct 16-byte bank groups whether the LDS services
-// 8 lanes (128 bytes) or 16 lanes (256 bytes) per pass: within any 8 rows the
-// even and the odd rows take distinct slots, and rows r, r+4, r+8, r+12
-// (same bank offset r*64 mod 256) take four distinct slots.
-__device__ __forceinline__ int swz_g(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
-__device__ __forceinline__ int swz(int r, int kc) { return kc ^ swz_g(r); }
+// Slot of 16-byte chunk kc (0..7) in 128-byte tile row r: kc ^ f(r) with
+// f(r) = (r ^ (r >> 3)) & 7.  A fragment read takes one chunk of 32
+// consecutive rows; the LDS serves it without bank conflicts whether it
+// handles 8 lanes (128 bytes) or 16 lanes (256 bytes) per pass: any 8
+// consecutive rows get 8 distinct slots, and of 16 consecutive rows from a
+// multiple of 16 the 8 even rows (one half of a 256-byte bank window) get 8
+// distinct slots, as do the 8 odd rows.
+__device__ __forceinline__ int swz_f(int r) { return (r ^ (r >> 3)) & 7; }
 
 // XCD-aware tile order: hardware hands workgroup w to XCD (w mod 8); give
 // each XCD one contiguous range of logical tiles (N fastest), so the N tiles
@@ -95,27 +101,35 @@ struct Frag;
 // Lane l holds column l % 32 and rows 8 q + 4 (l / 32) + r (element 4 q + r).
 typedef f32x16_t WaveAcc[4][4];
 
-// One K slab (64 bytes of every tile row) is consumed in two halves; a half
-// reads 4 A and 4 B fragments of 16 bytes per lane from LDS and issues the
-// MFMAs over them.  The 16-byte chunk a lane reads is chunk 2 half + l / 32
-// (bf16) or l / 32 * 2 + half (fp32) of its row, found at slot chunk ^ x.
+// A K slab (128 bytes of every tile row) is consumed in 4 steps; step s reads
+// 4 A and 4 B fragments of 16 bytes per lane from LDS (lane l: row l % 32 of
+// each 32-row subtile, chunk 2 s + l / 32 of the row) and issues the MFMAs
+// over them.  Rows 32 i + (l % 32) of subtile i have f = x0 ^ 4 (i & 1) with
+// x0 = (l & 7) ^ ((l >> 3) & 3), so chunk 2 s + h sits at byte
+// 16 (h ^ x0) ^ 32 (s ^ 2 (i & 1)) of the row: ro[k] holds the lane's row
+// start plus 16 (h ^ x0) ^ 32 k.
 struct Frags {
   f32x4_t a[4], b[4];
 };
 
+template <int S>
+__device__ __forceinline__ void read_frags(const char* As, const char* Bs, const int (&ro)[4], int wm, int wn,
+                                           Frags& f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int k = S ^ (2 * (i & 1));
+    f.a[i] = *reinterpret_cast<const f32x4_t*>(As + (wm * 128 + i * 32) * kRowBytes + ro[k]);
+    f.b[i] = *reinterpret_cast<const f32x4_t*>(Bs + (wn * 128 + i * 32) * kRowBytes + ro[k]);
+  }
+}
+
 template <>
 struct Frag<DT_BF16> {
-  // k16 step `half` of the 32 bf16 of a slab: lane l feeds row l % 32 and the
-  // 8 consecutive k of chunk 2 half + l / 32.
-  static __device__ __forceinline__ void load(const char* As, const char* Bs, int lane_off, int x, int h, int wm,
-                                              int wn, int half, Frags& f) {
-    const int slot = ((half * 2 + h) ^ x) * 16;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f.a[i] = *reinterpret_cast<const f32x4_t*>(As + (wm * 128 + i * 32) * kRowBytes + lane_off + slot);
-      f.b[i] = *reinterpret_cast<const f32x4_t*>(Bs + (wn * 128 + i * 32) * kRowBytes + lane_off + slot);
-    }
+  static __device__ __forceinline__ void mma1(const Frags& f, WaveAcc& acc, int i, int j) {
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f.a[i]),
+                                                         __builtin_bit_cast(bf16x8_t, f.b[j]), acc[i][j], 0, 0, 0);
   }
+  // Step s: lane l feeds row l % 32 and the 8 consecutive k of chunk 2 s + l / 32.
   // MFMAs of M subtiles [I0, I1) over all 4 N subtiles.
   template <int I0 = 0, int I1 = 4>
   static __device__ __forceinline__ void mma(const Frags& f, WaveAcc& acc) {
@@ -130,19 +144,13 @@ struct Frag<DT_BF16> {
 
 template <>
 struct Frag<DT_F32> {
-  // Half `half` of the 16 fp32 of a slab: four 32x32x2 MFMAs per (i, j).  At
-  // step t lane l feeds k = 8 (l / 32) + 4 half + t, so the two lane halves
-  // cover k and k + 8; the same permutation of k on both operands leaves the
-  // dot products unchanged.
-  static __device__ __forceinline__ void load(const char* As, const char* Bs, int lane_off, int x, int h, int wm,
-                                              int wn, int half, Frags& f) {
-    const int slot = ((h * 2 + half) ^ x) * 16;
+  static __device__ __forceinline__ void mma1(const Frags& f, WaveAcc& acc, int i, int j) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f.a[i] = *reinterpret_cast<const f32x4_t*>(As + (wm * 128 + i * 32) * kRowBytes + lane_off + slot);
-      f.b[i] = *reinterpret_cast<const f32x4_t*>(Bs + (wn * 128 + i * 32) * kRowBytes + lane_off + slot);
-    }
+    for (int t = 0; t < 4; ++t) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[i][t], f.b[j][t], acc[i][j], 0, 0, 0);
   }
+  // Step s: chunk 2 s + h holds the 4 fp32 k = 8 s + 4 h + t, t = 0..3; four
+  // 32x32x2 MFMAs per (i, j), where at MFMA t lane half h feeds k = 8 s + 4 h + t.
+  // The same permutation of k on both operands leaves the dot products unchanged.
   template <int I0 = 0, int I1 = 4>
   static __device__ __forceinline__ void mma(const Frags& f, WaveAcc& acc) {
 #pragma unroll
@@ -155,17 +163,25 @@ struct Frag<DT_F32> {
   }
 };
 
-// Copy one 64-byte-wide K slab of 256 rows of one operand into LDS.  Wave w
-// fills rows [64 w, 64 w + 64) with 4 instructions of 1 KiB (16 rows) each;
-// lane p writes LDS slot p & 3 of row p >> 2, which holds k-chunk
-// swz(row, p & 3) -- an XOR, so reads find chunk kc at swz(row, kc).
-__device__ __forceinline__ void load_slab(const char* base, const uint32_t (&off)[4], int64_t k_bytes, char* lds_tile,
-                                          int w) {
-  const char* kb = base + k_bytes;                  // uniform
+// Copy one 128-byte-wide K slab of 256 rows of one operand into LDS.  Wave w
+// fills rows [64 w, 64 w + 64) with 8 instructions of 1 KiB (8 rows) each;
+// lane p writes LDS slot p & 7 of row p >> 3 of its 8, which holds chunk
+// (p & 7) ^ f(row) -- an XOR, so reads find chunk kc at kc ^ f(row).  The 8
+// lanes of a row read its 128 bytes: one full cache line.  Buffer loads take
+// the operand base from a descriptor, the lane's row offset from a 32-bit
+// register and the slab's K offset from a scalar register.
+__device__ __forceinline__ void load_slab(__amdgpu_buffer_rsrc_t src, const uint32_t (&off)[kLoadsPerSlab],
+                                          uint32_t k_bytes, char* lds_slab, int w) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    __builtin_amdgcn_global_load_lds((const void*)(kb + off[i]), (lds_void_t*)(lds_tile + (w * 4 + i) * 1024), 16,
-                                     0, 0);
+  for (int i = 0; i < kLoadsPerSlab; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)(lds_slab + (w * 8 + i) * 1024), 16, off[i], k_bytes,
+                                             0, 0);
+}
+
+// Raw buffer descriptor over `base` (no stride, no range limit that the
+// 32-bit offsets could reach; dword 3 as for gfx9 raw buffers).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const char* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, -1, 0x00020000);
 }
 
 // s_waitcnt with vmcnt(n) and the other counters left open (gfx9 encoding:
@@ -186,18 +202,9 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
 // s_waitcnt lgkmcnt(0) with vmcnt and expcnt left open.
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
 
-// Wait until at most `n` slab loads (8 instructions each per wave: 4 for A,
-// 4 for B) are still in flight.
-__device__ __forceinline__ void wait_slabs_in_flight(int n) {
-  if (n >= 3) wait_vmcnt<24>();
-  else if (n == 2) wait_vmcnt<16>();
-  else if (n == 1) wait_vmcnt<8>();
-  else wait_vmcnt<0>();
-}
-
 // Workgroup barrier for the K loop.  __syncthreads() also fences global
 // memory, which makes the compiler wait for EVERY outstanding load (vmcnt(0))
-// and would drain the slab ring; here the caller waits for exactly the slab
+// and would drain the slab ring; here the caller waits for exactly the slabs
 // it needs, and the empty asm statements keep the compiler from moving LDS
 // accesses across the barrier.
 __device__ __forceinline__ void lds_barrier() {
@@ -206,86 +213,178 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// K loop over a ring of kStages LDS slabs: slab kt + kStages - 1 is
-// requested while slab kt is multiplied, so up to kStages - 1 slabs of
-// global -> LDS copies overlap the matrix work.  Within an iteration:
-//   copy request for slab kt + 4 | read half 1 of slab kt | MFMAs of half 0
-//   wait for slab kt + 1 (own copies) and own LDS reads | barrier
-//   read half 0 of slab kt + 1   | MFMAs of half 1
-// so LDS reads always overlap MFMAs.  After the barrier every wave's copies
-// of slab kt + 1 have landed and every wave has finished reading slab kt,
-// whose stage the next iteration refills.
+// State of the K loop of one wave.
+struct Ring {
+  __amdgpu_buffer_rsrc_t a_src;
+  __amdgpu_buffer_rsrc_t b_src;
+  char* lds;
+  int sa, sb;        // ring slots of the slab being multiplied
+  int w;
+};
+
+// Fragment r (0..7) of step S: A subtile r for r < 4, else B subtile r - 4.
+template <int S, int R>
+__device__ __forceinline__ void read_frag(const char* As, const char* Bs, const int (&ro)[4], int wm, int wn,
+                                          Frags& f) {
+  constexpr int i = R & 3;
+  constexpr int k = S ^ (2 * (i & 1));
+  if (R < 4) f.a[i] = *reinterpret_cast<const f32x4_t*>(As + (wm * 128 + i * 32) * kRowBytes + ro[k]);
+  else f.b[i] = *reinterpret_cast<const f32x4_t*>(Bs + (wn * 128 + i * 32) * kRowBytes + ro[k]);
+}
+
+// Slab copies of one iteration: copy q < 8 is row group q of the Wt slab,
+// q >= 8 row group q - 8 of the H slab.
+struct Copies {
+  __amdgpu_buffer_rsrc_t a_src, b_src;
+  char* a_dst;
+  char* b_dst;
+  uint32_t a_k, b_k;
+};
+
+template <int Q>
+__device__ __forceinline__ void issue_copy(const Copies& c, const uint32_t (&a_off)[kLoadsPerSlab],
+                                           const uint32_t (&b_off)[kLoadsPerSlab], int w) {
+  if (Q < 8)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.b_src, (lds_void_t*)(c.b_dst + (w * 8 + Q) * 1024), 16, b_off[Q & 7],
+                                             c.b_k, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.a_src, (lds_void_t*)(c.a_dst + (w * 8 + (Q & 7)) * 1024), 16,
+                                             a_off[Q & 7], c.a_k, 0, 0);
+}
+
+// One step: the 16 MFMAs over fragments `cur` (M subtile outer, N inner) with
+// the 8 reads of the next step's fragments (in the order that step consumes
+// them: a0 b0 b1 b2 b3 a1 a2 a3) issued after the first 8 MFMAs, and NQ
+// slab copies Q0, Q0 + 1, ... issued after every STRIDE-th MFMA.  Spreading
+// the copies keeps the texture address unit's queue from filling up (a full
+// queue stalls the issuing wave, MFMAs included).
+template <int DIN, int SN, bool READ, int Q0, int NQ, int STRIDE>
+__device__ __forceinline__ void step(const Frags& cur, Frags& nxt, WaveAcc& acc, const char* As, const char* Bs,
+                                     const int (&ro)[4], int wm, int wn, const Copies& cp,
+                                     const uint32_t (&a_off)[kLoadsPerSlab], const uint32_t (&b_off)[kLoadsPerSlab],
+                                     int w) {
+  constexpr int kOrder[8] = {0, 4, 5, 6, 7, 1, 2, 3};
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    Frag<DIN>::mma1(cur, acc, q >> 2, q & 3);
+    if (READ && q < 8) {
+      switch (q) {
+        case 0: read_frag<SN, kOrder[0]>(As, Bs, ro, wm, wn, nxt); break;
+        case 1: read_frag<SN, kOrder[1]>(As, Bs, ro, wm, wn, nxt); break;
+        case 2: read_frag<SN, kOrder[2]>(As, Bs, ro, wm, wn, nxt); break;
+        case 3: read_frag<SN, kOrder[3]>(As, Bs, ro, wm, wn, nxt); break;
+        case 4: read_frag<SN, kOrder[4]>(As, Bs, ro, wm, wn, nxt); break;
+        case 5: read_frag<SN, kOrder[5]>(As, Bs, ro, wm, wn, nxt); break;
+        case 6: read_frag<SN, kOrder[6]>(As, Bs, ro, wm, wn, nxt); break;
+        default: read_frag<SN, kOrder[7]>(As, Bs, ro, wm, wn, nxt); break;
+      }
+    }
+    if (NQ > 0 && q % STRIDE == 0 && q / STRIDE < NQ) {
+      switch (Q0 + q / STRIDE) {
+#define SEQCOMP_COPY_CASE(n) \
+  case n:                    \
+    issue_copy<n>(cp, a_off, b_off, w); \
+    break;
+        SEQCOMP_COPY_CASE(0) SEQCOMP_COPY_CASE(1) SEQCOMP_COPY_CASE(2) SEQCOMP_COPY_CASE(3)
+        SEQCOMP_COPY_CASE(4) SEQCOMP_COPY_CASE(5) SEQCOMP_COPY_CASE(6) SEQCOMP_COPY_CASE(7)
+        SEQCOMP_COPY_CASE(8) SEQCOMP_COPY_CASE(9) SEQCOMP_COPY_CASE(10) SEQCOMP_COPY_CASE(11)
+        SEQCOMP_COPY_CASE(12) SEQCOMP_COPY_CASE(13) SEQCOMP_COPY_CASE(14)
+        default: issue_copy<15>(cp, a_off, b_off, w); break;
+#undef SEQCOMP_COPY_CASE
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// One K slab j.  Slab j - 1 was finished by every wave before the barrier
+// that opened this iteration, so its slots take the copies of H slab j + 2
+// (3-slot ring) and Wt slab j + 1 (2-slot ring).  Per-wave copy order is
+// ... A(j+1) B(j+1) A(j+2)[0..3] | barrier | A(j+2)[4..7]: before the barrier
+// vmcnt(4) (the 4 copies of step 2 left open) means A(j+1) and B(j+1) have
+// landed.
+//   step 0 MFMAs | reads of step 1, Wt copies 0-3 in between
+//   step 1 MFMAs | reads of step 2, Wt copies 4-7 in between
+//   step 2 MFMAs | reads of step 3, H copies 0-3 in between
+//   wait copies + own reads | barrier
+//   step 3 MFMAs | reads of step 0 of slab j + 1, H copies 4-7 in between
+// The H copies issued after the barrier go to the slot of slab j - 1 too,
+// which every wave had finished before this iteration began.
+template <int DIN, bool ISSUE_B, bool ISSUE_A, bool LAST>
+__device__ __forceinline__ void k_iter(Ring& R, int j, const uint32_t (&a_off)[kLoadsPerSlab],
+                                       const uint32_t (&b_off)[kLoadsPerSlab], const int (&ro)[4], int wm, int wn,
+                                       Frags& f0, Frags& f1, WaveAcc& acc) {
+  const char* As = R.lds + R.sa * kSlabBytes;
+  const char* Bs = R.lds + kLdsB + R.sb * kSlabBytes;
+  Copies cp;
+  cp.a_src = R.a_src;
+  cp.b_src = R.b_src;
+  cp.b_dst = R.lds + kLdsB + (R.sb ^ 1) * kSlabBytes;
+  cp.a_dst = R.lds + (R.sa == 0 ? kStagesA - 1 : R.sa - 1) * kSlabBytes;
+  cp.b_k = (uint32_t)(j + 1) * kRowBytes;
+  cp.a_k = (uint32_t)(j + 2) * kRowBytes;
+  // Wt copies (needed at the end of this iteration) in steps 0 and 1, H
+  // copies (needed at the end of the next one) in steps 2 and 3.
+  constexpr int NB = ISSUE_B ? 4 : 0;
+  constexpr int NA = ISSUE_A ? 4 : 0;
+  __builtin_amdgcn_sched_barrier(0);
+  step<DIN, 1, true, 0, NB, 4>(f0, f1, acc, As, Bs, ro, wm, wn, cp, a_off, b_off, R.w);
+  step<DIN, 2, true, 4, NB, 4>(f1, f0, acc, As, Bs, ro, wm, wn, cp, a_off, b_off, R.w);
+  step<DIN, 3, true, 8, NA, 4>(f0, f1, acc, As, Bs, ro, wm, wn, cp, a_off, b_off, R.w);
+  if (!LAST) {
+    wait_vmcnt_lgkm0<NA>();                         // A(j+1), B(j+1) landed; the step-2 H copies may be open
+    lds_barrier();
+    R.sa = R.sa == kStagesA - 1 ? 0 : R.sa + 1;
+    R.sb ^= 1;
+    step<DIN, 0, true, 12, NA, 4>(f1, f0, acc, R.lds + R.sa * kSlabBytes, R.lds + kLdsB + R.sb * kSlabBytes, ro, wm,
+                                  wn, cp, a_off, b_off, R.w);
+  } else {
+    wait_lgkmcnt0();   // every wave is done with the ring before the epilogue reuses the LDS
+    lds_barrier();
+    step<DIN, 0, false, 0, 0, 1>(f1, f0, acc, As, Bs, ro, wm, wn, cp, a_off, b_off, R.w);
+  }
+}
+
 template <int DIN>
-__device__ __forceinline__ void mainloop(const char* a_base, const uint32_t (&a_off)[4], const char* b_base,
-                                         const uint32_t (&b_off)[4], int nk, char* lds, int w, int lane, int wm,
-                                         int wn, WaveAcc& acc) {
-  const int lane_off = (lane & 31) * kRowBytes;
-  const int x = swz_g(lane & 31);                   // swz() of rows 32 k + (lane & 31)
-  const int h = lane >> 5;
+__device__ __forceinline__ void mainloop(const char* a_base, const uint32_t (&a_off)[kLoadsPerSlab],
+                                         const char* b_base, const uint32_t (&b_off)[kLoadsPerSlab], int nk,
+                                         char* lds, int w, int lane, int wm, int wn, WaveAcc& acc) {
+  const __amdgpu_buffer_rsrc_t a_src = raw_rsrc(a_base), b_src = raw_rsrc(b_base);
+  int ro[4];
+  {
+    const int h = lane >> 5;
+    const int x0 = (lane & 7) ^ ((lane >> 3) & 3);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) ro[k] = (lane & 31) * kRowBytes + ((16 * (h ^ x0)) ^ (32 * k));
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
 
-  const int pro = min(kStages - 1, nk);
-  for (int s = 0; s < pro; ++s) {
-    load_slab(a_base, a_off, (int64_t)s * kRowBytes, lds + s * kStageBytes, w);
-    load_slab(b_base, b_off, (int64_t)s * kRowBytes, lds + s * kStageBytes + kTileBytes, w);
+  Ring R{a_src, b_src, lds, 0, 0, w};
+  load_slab(a_src, a_off, 0, lds, w);
+  load_slab(b_src, b_off, 0, lds + kLdsB, w);
+  if (nk > 1) {
+    load_slab(a_src, a_off, kRowBytes, lds + kSlabBytes, w);
+    wait_vmcnt<kLoadsPerSlab>();                    // A(0), B(0) landed; A(1) in flight
+  } else {
+    wait_vmcnt<0>();
   }
-  wait_slabs_in_flight(pro - 1);                    // slab 0 has landed
   lds_barrier();
   Frags f0, f1;
-  Frag<DIN>::load(lds, lds + kTileBytes, lane_off, x, h, wm, wn, 0, f0);
-  int stage = 0;
-  int kt = 0;
-  // steady state: slab kt + kStages - 1 exists (so does slab kt + 1).  The
-  // compiler waits for all LDS reads before the first MFMA that uses the
-  // fragments carried over the loop edge (f0), so half 1 is read only after
-  // that first MFMA group: the forced wait then covers reads issued a whole
-  // MFMA block earlier, and the half-1 reads overlap 12 MFMAs.
-  for (; kt + kStages - 1 < nk; ++kt) {
-    char* cur = lds + stage * kStageBytes;
-    const int nxt_stage = stage + 1 == kStages ? 0 : stage + 1;
-    char* dst = lds + (stage == 0 ? kStages - 1 : stage - 1) * kStageBytes;   // read in iteration kt - 1
-    const int64_t kb = (int64_t)(kt + kStages - 1) * kRowBytes;
-    load_slab(a_base, a_off, kb, dst, w);
-    load_slab(b_base, b_off, kb, dst + kTileBytes, w);
-    __builtin_amdgcn_sched_barrier(0);
-    Frag<DIN>::template mma<0, 1>(f0, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    Frag<DIN>::load(cur, cur + kTileBytes, lane_off, x, h, wm, wn, 1, f1);
-    __builtin_amdgcn_sched_barrier(0);
-    Frag<DIN>::template mma<1, 4>(f0, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt_lgkm0<8 * (kStages - 2)>();          // slab kt + 1 landed (kt + 2 .. kt + 4 in flight), own reads done
-    lds_barrier();
-    char* nx = lds + nxt_stage * kStageBytes;
-    Frag<DIN>::load(nx, nx + kTileBytes, lane_off, x, h, wm, wn, 0, f0);
-    __builtin_amdgcn_sched_barrier(0);
-    Frag<DIN>::mma(f1, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    stage = nxt_stage;
+  read_frags<0>(lds, lds + kLdsB, ro, wm, wn, f0);
+  int j = 0;
+  for (; j + 2 < nk; ++j) k_iter<DIN, true, true, false>(R, j, a_off, b_off, ro, wm, wn, f0, f1, acc);
+  if (j + 1 < nk) {
+    k_iter<DIN, true, false, false>(R, j, a_off, b_off, ro, wm, wn, f0, f1, acc);
+    ++j;
   }
-  // drain: every slab has been requested
-  for (; kt < nk; ++kt) {
-    char* cur = lds + stage * kStageBytes;
-    const int nxt_stage = stage + 1 == kStages ? 0 : stage + 1;
-    Frag<DIN>::load(cur, cur + kTileBytes, lane_off, x, h, wm, wn, 1, f1);
-    Frag<DIN>::mma(f0, acc);
-    wait_slabs_in_flight(nk - 2 - kt);
-    wait_lgkmcnt0();
-    lds_barrier();
-    if (kt + 1 < nk) {
-      char* nx = lds + nxt_stage * kStageBytes;
-      Frag<DIN>::load(nx, nx + kTileBytes, lane_off, x, h, wm, wn, 0, f0);
-    }
-    Frag<DIN>::mma(f1, acc);
-    stage = nxt_stage;
-  }
+  k_iter<DIN, false, false, true>(R, j, a_off, b_off, ro, wm, wn, f0, f1, acc);
 }
 
 // Per-thread source rows of the two operands: thread (wave w, lane p) loads
-// tile rows r_i = 64 w + 16 i + (p >> 2), i = 0..3, at k-chunk swz(r_i, p & 3).
+// tile rows r_i = 64 w + 8 i + (p >> 3), i = 0..7, at chunk (p & 7) ^ f(r_i).
 template <int MODE>
 __device__ __forceinline__ int b_row_of(int n, int nt, int c, int n_out) {
   if (MODE == MODE_PROJECT) return min(nt * kTile + n, n_out - 1);
@@ -507,7 +606,7 @@ template <int DIN, int MODE, int DOUT>
 __device__ __forceinline__ void run_tile(const Args& a, int L, char* lds) {
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
-  const int w = tid >> 6, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int mt = L / a.n_nt, nt = L - mt * a.n_nt;
   const int wm = w >> 1, wn = w & 1;
 
@@ -525,11 +624,11 @@ __device__ __forceinline__ void run_tile(const Args& a, int L, char* lds) {
   // Byte offsets from uniform bases; they fit 32 bits because a tile of H is
   // 256 rows of at most 64 KiB and the host rejects a Wt of 4 GiB or more.
   const char* a_base = a.H + row0 * a.lda;
-  uint32_t a_off[4], b_off[4];
+  uint32_t a_off[kLoadsPerSlab], b_off[kLoadsPerSlab];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = w * 64 + i * 16 + (lane >> 2);
-    const int kc = swz(r, lane & 3);
+  for (int i = 0; i < kLoadsPerSlab; ++i) {
+    const int r = w * 64 + i * 8 + (lane >> 3);
+    const int kc = (lane & 7) ^ swz_f(r);
     a_off[i] = (uint32_t)(min(r, nvalid - 1) * a.lda + kc * 16);
     b_off[i] = (uint32_t)((int64_t)b_row_of<MODE>(r, nt, a.c, a.n_out) * a.lda + kc * 16);
   }

@@ -161,3 +161,6 @@ def test_project_rejects_bad_arguments(lib):
     assert f(0, 64, 64, _lib.BF16, B_, 128, OUT, 128, _lib.BF16, None) == S["SEQCOMP_E_NULL"]
     assert f(A, 64, 64, _lib.BF16, B_, 128, A + 64, 128, _lib.BF16, None) == S["SEQCOMP_E_ALIAS"]
     assert f(A, 0, 64, _lib.BF16, B_, 128, 0, 128, _lib.BF16, None) == S["SEQCOMP_OK"]
+    # a 256-row tile of H must stay addressable with 32-bit byte offsets
+    assert f(A, 64, 1 << 22, _lib.F32, B_, 16, OUT, 16, _lib.F32, None) == S["SEQCOMP_E_UNSUPPORTED"]
+    assert fused(lib, d=1 << 22, c=16, in_dt=_lib.F32) == S["SEQCOMP_E_UNSUPPORTED"]
