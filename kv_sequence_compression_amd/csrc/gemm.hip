@@ -252,23 +252,30 @@ __device__ __forceinline__ void issue_copy(const Copies& c, const uint32_t (&a_o
                                              a_off[Q & 7], c.a_k, 0, 0);
 }
 
-// One step: the 16 MFMAs over fragments `cur` (M subtile outer, N inner) with
-// the 8 reads of the next step's fragments (in the order that step consumes
-// them: a0 b0 b1 b2 b3 a1 a2 a3) issued after the first 8 MFMAs, and NQ
-// slab copies Q0, Q0 + 1, ... issued after every STRIDE-th MFMA.  Spreading
-// the copies keeps the texture address unit's queue from filling up (a full
-// queue stalls the issuing wave, MFMAs included).
-template <int DIN, int SN, bool READ, int Q0, int NQ, int STRIDE>
+// One step: the 16 MFMAs over fragments `cur` (M subtile outer, N inner),
+// with the 8 reads of the next step's fragments (in the order that step
+// consumes them: a0 b0 b1 b2 b3 a1 a2 a3) issued after the MFMAs whose bit is
+// set in RMASK, and slab copies Q0, Q0 + 1, ... after those set in CMASK.  A
+// copy occupies the issuing wave for ~16 cycles (64 lanes x 16 bytes through
+// the address unit), so copies and reads go into different MFMA shadows.
+__host__ __device__ constexpr int popc16(int x) {
+  return ((x >> 0) & 1) + ((x >> 1) & 1) + ((x >> 2) & 1) + ((x >> 3) & 1) + ((x >> 4) & 1) + ((x >> 5) & 1) +
+         ((x >> 6) & 1) + ((x >> 7) & 1) + ((x >> 8) & 1) + ((x >> 9) & 1) + ((x >> 10) & 1) + ((x >> 11) & 1) +
+         ((x >> 12) & 1) + ((x >> 13) & 1) + ((x >> 14) & 1) + ((x >> 15) & 1);
+}
+
+template <int DIN, int SN, int RMASK, int Q0, int CMASK>
 __device__ __forceinline__ void step(const Frags& cur, Frags& nxt, WaveAcc& acc, const char* As, const char* Bs,
                                      const int (&ro)[4], int wm, int wn, const Copies& cp,
                                      const uint32_t (&a_off)[kLoadsPerSlab], const uint32_t (&b_off)[kLoadsPerSlab],
                                      int w) {
+  static_assert(RMASK == 0 || popc16(RMASK) == 8, "a step reads 8 fragments");
   constexpr int kOrder[8] = {0, 4, 5, 6, 7, 1, 2, 3};
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     Frag<DIN>::mma1(cur, acc, q >> 2, q & 3);
-    if (READ && q < 8) {
-      switch (q) {
+    if ((RMASK >> q) & 1) {
+      switch (popc16(RMASK & ((1 << q) - 1))) {
         case 0: read_frag<SN, kOrder[0]>(As, Bs, ro, wm, wn, nxt); break;
         case 1: read_frag<SN, kOrder[1]>(As, Bs, ro, wm, wn, nxt); break;
         case 2: read_frag<SN, kOrder[2]>(As, Bs, ro, wm, wn, nxt); break;
@@ -279,8 +286,8 @@ __device__ __forceinline__ void step(const Frags& cur, Frags& nxt, WaveAcc& acc,
         default: read_frag<SN, kOrder[7]>(As, Bs, ro, wm, wn, nxt); break;
       }
     }
-    if (NQ > 0 && q % STRIDE == 0 && q / STRIDE < NQ) {
-      switch (Q0 + q / STRIDE) {
+    if ((CMASK >> q) & 1) {
+      switch (Q0 + popc16(CMASK & ((1 << q) - 1))) {
 #define SEQCOMP_COPY_CASE(n) \
   case n:                    \
     issue_copy<n>(cp, a_off, b_off, w); \
@@ -297,17 +304,21 @@ __device__ __forceinline__ void step(const Frags& cur, Frags& nxt, WaveAcc& acc,
   }
 }
 
+// MFMA slots of the fragment reads and of the 4 copies of a step.
+constexpr int kReadSlots = 0x00ff;    // after MFMAs 0..7
+constexpr int kCopySlots = 0x5500;    // after MFMAs 8, 10, 12, 14
+
 // One K slab j.  Slab j - 1 was finished by every wave before the barrier
 // that opened this iteration, so its slots take the copies of H slab j + 2
 // (3-slot ring) and Wt slab j + 1 (2-slot ring).  Per-wave copy order is
 // ... A(j+1) B(j+1) A(j+2)[0..3] | barrier | A(j+2)[4..7]: before the barrier
 // vmcnt(4) (the 4 copies of step 2 left open) means A(j+1) and B(j+1) have
 // landed.
-//   step 0 MFMAs | reads of step 1, Wt copies 0-3 in between
-//   step 1 MFMAs | reads of step 2, Wt copies 4-7 in between
-//   step 2 MFMAs | reads of step 3, H copies 0-3 in between
+//   step 0 MFMAs | reads of step 1, then Wt copies 0-3, in between
+//   step 1 MFMAs | reads of step 2, then Wt copies 4-7, in between
+//   step 2 MFMAs | reads of step 3, then H copies 0-3, in between
 //   wait copies + own reads | barrier
-//   step 3 MFMAs | reads of step 0 of slab j + 1, H copies 4-7 in between
+//   step 3 MFMAs | reads of step 0 of slab j + 1, then H copies 4-7, in between
 // The H copies issued after the barrier go to the slot of slab j - 1 too,
 // which every wave had finished before this iteration began.
 template <int DIN, bool ISSUE_B, bool ISSUE_A, bool LAST>
@@ -325,23 +336,24 @@ __device__ __forceinline__ void k_iter(Ring& R, int j, const uint32_t (&a_off)[k
   cp.a_k = (uint32_t)(j + 2) * kRowBytes;
   // Wt copies (needed at the end of this iteration) in steps 0 and 1, H
   // copies (needed at the end of the next one) in steps 2 and 3.
-  constexpr int NB = ISSUE_B ? 4 : 0;
-  constexpr int NA = ISSUE_A ? 4 : 0;
+  constexpr int CB = ISSUE_B ? kCopySlots : 0;
+  constexpr int CA = ISSUE_A ? kCopySlots : 0;
+  constexpr int NA = popc16(CA);                    // H copies issued before the barrier
   __builtin_amdgcn_sched_barrier(0);
-  step<DIN, 1, true, 0, NB, 4>(f0, f1, acc, As, Bs, ro, wm, wn, cp, a_off, b_off, R.w);
-  step<DIN, 2, true, 4, NB, 4>(f1, f0, acc, As, Bs, ro, wm, wn, cp, a_off, b_off, R.w);
-  step<DIN, 3, true, 8, NA, 4>(f0, f1, acc, As, Bs, ro, wm, wn, cp, a_off, b_off, R.w);
+  step<DIN, 1, kReadSlots, 0, CB>(f0, f1, acc, As, Bs, ro, wm, wn, cp, a_off, b_off, R.w);
+  step<DIN, 2, kReadSlots, popc16(CB), CB>(f1, f0, acc, As, Bs, ro, wm, wn, cp, a_off, b_off, R.w);
+  step<DIN, 3, kReadSlots, 8, CA>(f0, f1, acc, As, Bs, ro, wm, wn, cp, a_off, b_off, R.w);
   if (!LAST) {
     wait_vmcnt_lgkm0<NA>();                         // A(j+1), B(j+1) landed; the step-2 H copies may be open
     lds_barrier();
     R.sa = R.sa == kStagesA - 1 ? 0 : R.sa + 1;
     R.sb ^= 1;
-    step<DIN, 0, true, 12, NA, 4>(f1, f0, acc, R.lds + R.sa * kSlabBytes, R.lds + kLdsB + R.sb * kSlabBytes, ro, wm,
-                                  wn, cp, a_off, b_off, R.w);
+    step<DIN, 0, kReadSlots, 8 + NA, CA>(f1, f0, acc, R.lds + R.sa * kSlabBytes, R.lds + kLdsB + R.sb * kSlabBytes,
+                                         ro, wm, wn, cp, a_off, b_off, R.w);
   } else {
     wait_lgkmcnt0();   // every wave is done with the ring before the epilogue reuses the LDS
     lds_barrier();
-    step<DIN, 0, false, 0, 0, 1>(f1, f0, acc, As, Bs, ro, wm, wn, cp, a_off, b_off, R.w);
+    step<DIN, 0, 0, 0, 0>(f1, f0, acc, As, Bs, ro, wm, wn, cp, a_off, b_off, R.w);
   }
 }
 
