@@ -7,7 +7,7 @@ computation runs in the HIP kernels of ``libseqcomp.so``.
 
 Functions (each returns torch tensors on the inputs' device):
 
-* ``project(H, Wt, out_dtype)``                         -> Y = H Wt^T
+* ``project(H, Wt, out_dtype, out=None)``               -> Y = H Wt^T
 * ``pool_csa(Ca, Cb, Za, Zb, Ba, Bb, m, cu_seqlens, out_dtype)`` -> (entries, scale|None)
 * ``pool_hca(C, Z, B, m, cu_seqlens, out_dtype)``       -> (entries, scale|None)
 * ``compress_fused(mode, H, Wt, Ba, Bb, m, cu_seqlens, out_dtype)`` -> (entries, scale|None)
@@ -110,12 +110,21 @@ def _alloc_ws(nbytes: int, device):
     return torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=device)
 
 
-def project(H: torch.Tensor, Wt: torch.Tensor, out_dtype: str = "bf16") -> torch.Tensor:
-    """Y[T x n_out] = H[T x d] Wt[n_out x d]^T (eq. attn-seqcomp-csa-proj, all streams at once)."""
+def project(H: torch.Tensor, Wt: torch.Tensor, out_dtype: str = "bf16", out: torch.Tensor = None) -> torch.Tensor:
+    """Y[T x n_out] = H[T x d] Wt[n_out x d]^T (eq. attn-seqcomp-csa-proj, all streams at once).
+
+    `out`, if given, is a [T x n_out] view with unit column stride and any row
+    stride >= n_out (e.g. the left columns of a wider buffer); it is written
+    in place and returned."""
     T, d = H.shape
     n_out = Wt.shape[0]
-    Y = torch.empty((T, n_out), dtype=_TORCH_OUT[out_dtype], device=H.device)
-    _check(lib().seqcomp_project(_ptr(H), T, d, _in_code(H), _ptr(Wt), n_out, _ptr(Y), n_out,
+    if out is None:
+        Y = torch.empty((T, n_out), dtype=_TORCH_OUT[out_dtype], device=H.device)
+    else:
+        if out.shape != (T, n_out) or out.stride(1) != 1 or out.dtype != _TORCH_OUT[out_dtype]:
+            raise ValueError(f"out must be a [{T} x {n_out}] {_TORCH_OUT[out_dtype]} view with unit column stride")
+        Y = out
+    _check(lib().seqcomp_project(_ptr(H), T, d, _in_code(H), _ptr(Wt), n_out, _ptr(Y), Y.stride(0),
                                  _DT_CODE[out_dtype], _stream(H.device)), "seqcomp_project")
     return Y
 

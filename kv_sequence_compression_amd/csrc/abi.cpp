@@ -252,6 +252,8 @@ int seqcomp_project(const void* H, int64_t T, int64_t d, int in_dtype, const voi
   // the kernels address one 256-row tile of H and all of Wt with 32-bit byte offsets
   if (n_out * d * elt_size(in_dtype) >= (int64_t(1) << 32) || 256 * d * elt_size(in_dtype) >= (int64_t(1) << 32))
     return SEQCOMP_E_UNSUPPORTED;
+  // ... and store one 256-row tile of Y through offsets below 2^31
+  if (256 * ld_y * elt_size(out_dtype) >= (int64_t(1) << 31)) return SEQCOMP_E_UNSUPPORTED;
   if (T == 0) return SEQCOMP_OK;
   if (!H || !Wt || !Y) return SEQCOMP_E_NULL;
   if (!aligned16(H) || !aligned16(Wt) || !aligned16(Y)) return SEQCOMP_E_ALIGN;

@@ -457,21 +457,45 @@ __device__ __forceinline__ void store1(char* out, int64_t idx, float v) {
   else reinterpret_cast<float*>(out)[idx] = v;
 }
 
+// Projection epilogue: every accumulator element goes straight to Y through
+// a buffer descriptor over the tile's rows; rows past T fall outside the
+// descriptor's range and columns past n_out get an offset outside it, so the
+// hardware drops those stores and no branch splits the epilogue (branches
+// would let the compiler copy all 256 accumulators to VGPRs at once).
 template <int DOUT>
 __device__ void epilogue_project(const Args& a, WaveAcc& acc, int mt, int nt, int lane, int wm, int wn) {
+  constexpr int es = DOUT == DT_BF16 ? 2 : 4;
+  const int64_t row0 = (int64_t)mt * kTile;
+  const int64_t rows = min<int64_t>(kTile, a.T - row0);
+  const uint32_t range = (uint32_t)(rows * a.ld_y * es);   // < 2^31: checked by the host
+  const __amdgpu_buffer_rsrc_t dst =
+      __builtin_amdgcn_make_buffer_rsrc(a.Y + row0 * a.ld_y * es, (short)0, (int)range, 0x00020000);
   const int col = lane & 31, h = lane >> 5;
+  const uint32_t ld_bytes = (uint32_t)(a.ld_y * es);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int n = nt * kTile + wn * 128 + j * 32 + col;
-      if (n >= a.n_out) continue;
+      // 2^31 + (row offset < 2^31: checked by the host) is past the range
+      const uint32_t cbase = n < a.n_out ? (uint32_t)n * es : 0x80000000u;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int64_t row = (int64_t)mt * kTile + wm * 128 + i * 32 + (e >> 2) * 8 + h * 4 + (e & 3);
-        if (row < a.T) store1<DOUT>(a.Y, row * a.ld_y + n, acc[i][j][e]);
+        const uint32_t r = wm * 128 + i * 32 + (e >> 2) * 8 + h * 4 + (e & 3);
+        const uint32_t off = r * ld_bytes + cbase;
+        if (DOUT == DT_BF16) {
+          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f32_to_bf16_bits(acc[i][j][e]), dst, off, 0, 0);
+        } else {
+          // Pass the element through a VGPR: folding the accumulator register
+          // straight into the store's data operand stored element 0 sixteen
+          // times with this compiler.
+          float v = acc[i][j][e];
+          asm volatile("" : "+v"(v));
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, v), dst, off, 0, 0);
+        }
       }
     }
+    __builtin_amdgcn_sched_barrier(0);   // bounds the accumulator values held in VGPRs
   }
 }
 
@@ -537,22 +561,27 @@ __device__ void epilogue_csa(const Args& a, WaveAcc& acc, const TileRec& t, int 
       const SoftAcc prev = h ? px : carry;
       carry = px;
       const int blk = wm * 32 + ms * 8 + q * 2 + h;  // block (= entry) index inside the tile
-      if (ok && blk * 4 < t.n_rows) {
-        const int64_t e = (int64_t)t.entry_start + blk;
-        if (blk == 0) {
-          if (t.flags & TILE_FIRST) {
-            store1<DOUT>(a.out, e * c + ch, pa.A / pa.S);   // entry 0: no b rows
-          } else {
-            halo[0 * c + ch] = pa.M;
-            halo[1 * c + ch] = pa.S;
-            halo[2 * c + ch] = pa.A;
-          }
-        } else {
-          const SoftAcc m = softacc_merge(pa, prev);
-          store1<DOUT>(a.out, e * c + ch, m.A / m.S);
+      // The tile's block 0 has no b-partial here (lane h = 0 of wave row 0
+      // carries the empty partial), so the merge returns its a-partial: the
+      // whole entry when the tile starts its sequence (eq.
+      // attn-seqcomp-overlap-bound), else the halo's a-part.  Only the stores
+      // are predicated, so the arithmetic stays in one basic block.
+      const SoftAcc m = softacc_merge(pa, prev);
+      const bool first = (ms == 0 && q == 0) && blk == 0;
+      const bool tile_first = (t.flags & TILE_FIRST) != 0;
+      if (ok && blk * 4 < t.n_rows && (!first || tile_first))
+        store1<DOUT>(a.out, ((int64_t)t.entry_start + blk) * c + ch, m.A / m.S);
+      if (ms == 0 && q == 0) {
+        if (ok && first && !tile_first) {
+          halo[0 * c + ch] = pa.M;
+          halo[1 * c + ch] = pa.S;
+          halo[2 * c + ch] = pa.A;
         }
       }
     }
+    // Keep the accumulator reads of the next subtile row after this one:
+    // hoisted all at once they would need 256 VGPRs and spill.
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 

@@ -164,3 +164,5 @@ def test_project_rejects_bad_arguments(lib):
     # a 256-row tile of H must stay addressable with 32-bit byte offsets
     assert f(A, 64, 1 << 22, _lib.F32, B_, 16, OUT, 16, _lib.F32, None) == S["SEQCOMP_E_UNSUPPORTED"]
     assert fused(lib, d=1 << 22, c=16, in_dt=_lib.F32) == S["SEQCOMP_E_UNSUPPORTED"]
+    # ... and a 256-row tile of Y too
+    assert f(A, 64, 64, _lib.BF16, B_, 16, OUT, 1 << 22, _lib.BF16, None) == S["SEQCOMP_E_UNSUPPORTED"]

@@ -89,6 +89,20 @@ def test_project_bf16_ragged(gpu_device):
     assert row_rel_err(to64(Y), ref).max() <= 1e-5      # exact bf16 products, fp32 sums
 
 
+@pytest.mark.parametrize("od", ["f32", "bf16"])
+def test_project_into_padded_rows(gpu_device, od):
+    """Y as the left columns of a wider buffer (row stride > n_out), ragged T
+    and n_out: the padding columns and the rows past T keep their sentinel."""
+    T, d, n_out, ld = 300, 128, 272, 272 + 56
+    H = synth.normal((T, d), 1.0, (9, 1), gpu_device, "bf16")
+    Wt = synth.normal((n_out, d), 1.0 / np.sqrt(d), (9, 2), gpu_device, "bf16")
+    buf = torch.full((T + 5, ld), 7.0, dtype=torch.float32 if od == "f32" else torch.bfloat16, device=gpu_device)
+    Y = sc.project(H, Wt, od, out=buf[:T, :n_out])
+    ref = oracle.project(to64(H), to64(Wt).T)
+    assert row_rel_err(to64(Y), ref).max() <= 2e-2
+    assert bool((buf[:T, n_out:] == 7.0).all()) and bool((buf[T:] == 7.0).all())
+
+
 # -------------------------------------------------------------- fused, fp32
 
 def test_fused_csa_tiny_config(gpu_device):
