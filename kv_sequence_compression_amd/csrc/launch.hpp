@@ -9,11 +9,12 @@
 
 namespace seqcomp {
 
-// Rows per tile of the pooling kernels and of the fused kernels.
 // Rows per tile of the pooling kernels: CSA (m <= 16) takes as many whole
-// blocks as fit in 256 rows; HCA (m <= 256) takes 4 blocks, one per wave.
+// blocks as fit in 256 rows; HCA (m <= 256) takes whole blocks of about 1024
+// rows, a multiple of 4 blocks (the 4 waves of a workgroup share them and the
+// bias slice staged once for all of them).
 inline int pool_csa_tile_rows(int m) { return m * (256 / m); }
-inline int pool_hca_tile_rows(int m) { return 4 * m; }
+inline int pool_hca_tile_rows(int m) { return m * 4 * ((1024 / m + 3) / 4); }
 constexpr int kPoolCsaMaxM = 16;
 constexpr int kPoolHcaMaxM = 256;
 constexpr int kFusedTileRows = 256;   // MFMA macro-tile height (tokens)

@@ -61,22 +61,45 @@ __device__ __forceinline__ float raw_get(const Raw8<DIN>& r, int j) {
 }
 
 // Stage rows [0, m) of a bias slice (channels [ch0, ch0 + width)) into LDS as
-// log2(e) * B, row stride `width`.  All threads of the block take part.
+// log2(e) * B, row stride `width`.  All threads of the block take part; each
+// issues 4 independent 16-byte loads (indices past the end re-read the last
+// element) before its first store, so the staging costs a few memory
+// latencies instead of one per element.
 __device__ __forceinline__ void stage_bias(lds_f32* dst, const float* __restrict__ B, int m, int c, int ch0,
                                            int width) {
-  for (int i = threadIdx.x; i < m * width; i += blockDim.x) {
-    const int r = i / width, j = i - r * width;
-    const int ch = ch0 + j;
-    dst[i] = ch < c ? B[(int64_t)r * c + ch] * kLog2e : 0.f;
+  const int w4 = width >> 2;                       // c % 16 == 0 and ch0 % 64 == 0: 16-byte aligned
+  const int n4 = m * w4;
+  for (int base = 0; base < n4; base += 4 * kPoolThreads) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = min(base + u * kPoolThreads + (int)threadIdx.x, n4 - 1);
+      const int r = i / w4, j = i - r * w4;
+      v[u] = *reinterpret_cast<const float4*>(B + (int64_t)r * c + ch0 + 4 * j);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = base + u * kPoolThreads + (int)threadIdx.x;
+      if (i < n4) {
+        const int r = i / w4, j = i - r * w4;
+        lds_f32* d = dst + r * width + 4 * j;
+        d[0] = v[u].x * kLog2e;
+        d[1] = v[u].y * kLog2e;
+        d[2] = v[u].z * kLog2e;
+        d[3] = v[u].w * kLog2e;
+      }
+    }
   }
 }
 
 // Fold 8 rows of 8 channels into the online softmax state with ONE rescale.
-// Row k takes part iff bit k of `valid` is set; the others were loaded from a
-// valid row (finite values) and get logit -inf, hence weight exactly 0, so
-// the code has no branches.  Two passes over the rows (maximum, then
-// exponentials and sums) recompute the logit from the raw 16-byte loads and
-// the LDS bias instead of keeping 64 logits live.
+// Row k takes part iff bit k of `valid` is set (at least one is); the others
+// were loaded from a valid row (finite values) and get logit -inf, hence
+// weight exactly 0, so the code has no branches.  Two passes over the rows
+// (maximum, then exponentials and sums) recompute the logit from the raw
+// 16-byte loads and the LDS bias instead of keeping 64 logits live.  (A
+// separate unmasked path for full chunks raises the register count past the
+// 3-waves-per-SIMD limit and measured slower.)
 template <int DIN>
 __device__ __forceinline__ void fold_chunk(SoftAcc (&acc)[8], const Raw8<DIN> (&z)[8], const Raw8<DIN> (&v)[8],
                                            const lds_f32* const (&bias)[8], uint32_t valid) {
@@ -181,8 +204,8 @@ __global__ __launch_bounds__(kPoolThreads) void pool_csa_kernel(
   }
 }
 
-// HCA: workgroup = (64-channel slice, tile of 4 entries); wave w takes entry
-// w of the tile.  Lane = 8 g + v: vector v (8 channels) of the slice and row
+// HCA: workgroup = (64-channel slice, tile of entries); wave w takes entries
+// w, w + 4, ... of the tile (the bias slice is staged once for all of them).  Lane = 8 g + v: vector v (8 channels) of the slice and row
 // group g, which folds rows g, g + 8, g + 16, ... (so one load instruction
 // reads 8 consecutive rows); three butterfly merges combine the row groups.
 template <int DIN, int DOUT>
@@ -202,42 +225,44 @@ __global__ __launch_bounds__(kPoolThreads) void pool_hca_kernel(
   stage_bias(sB, B, m, c, ch0, width);
   __syncthreads();
   const int lane = threadIdx.x & 63;
-  const int e = threadIdx.x >> 6;
+  const int w = threadIdx.x >> 6;
   const int g = lane >> 3, v = lane & 7;
-  if (e * m >= t.n_rows) return;                  // this tile has fewer entries (no barrier follows)
   const bool vok = v * 8 < width;
   const int vv = vok ? v : 0;                     // lanes past the slice re-read vector 0, store nothing
-  const int64_t r_first = (int64_t)t.row_start + (int64_t)e * m;
   const int64_t col = (int64_t)(ch0 + vv * 8) * ES;
-  SoftAcc acc[8];
+  const int ne = t.n_rows / m;
+  for (int e = w; e < ne; e += 4) {               // entries w, w + 4, ... of the tile
+    const int64_t r_first = (int64_t)t.row_start + (int64_t)e * m;
+    SoftAcc acc[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) softacc_init(acc[j]);
+    for (int j = 0; j < 8; ++j) softacc_init(acc[j]);
 #pragma unroll 1
-  for (int r0 = g; r0 < m; r0 += 64) {            // this lane's rows r0, r0 + 8, ..., r0 + 56
-    Raw8<DIN> z[8], x[8];
-    const lds_f32* bias[8];
-    uint32_t valid = 0;
+    for (int r0 = g; r0 < m; r0 += 64) {          // this lane's rows r0, r0 + 8, ..., r0 + 56
+      Raw8<DIN> z[8], x[8];
+      const lds_f32* bias[8];
+      uint32_t valid = 0;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int r = r0 + 8 * k;
-      valid |= (r < m ? 1u : 0u) << k;
-      const int rr = min(r, m - 1);               // rows past the block re-read its last row, masked off
-      const int64_t row = r_first + rr;
-      ld_raw<DIN>(z[k], Z + row * ld_bytes + col);
-      ld_raw<DIN>(x[k], C + row * ld_bytes + col);
-      bias[k] = &sB[rr * width + vv * 8];
+      for (int k = 0; k < 8; ++k) {
+        const int r = r0 + 8 * k;
+        valid |= (r < m ? 1u : 0u) << k;
+        const int rr = min(r, m - 1);             // rows past the block re-read its last row, masked off
+        const int64_t row = r_first + rr;
+        ld_raw<DIN>(z[k], Z + row * ld_bytes + col);
+        ld_raw<DIN>(x[k], C + row * ld_bytes + col);
+        bias[k] = &sB[rr * width + vv * 8];
+      }
+      fold_chunk<DIN>(acc, z, x, bias, valid);
     }
-    fold_chunk<DIN>(acc, z, x, bias, valid);
-  }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    SoftAcc s = acc[j];
+    for (int j = 0; j < 8; ++j) {
+      SoftAcc s = acc[j];
 #pragma unroll
-    for (int mask = 8; mask <= 32; mask <<= 1)
-      s = softacc_merge(s, SoftAcc{__shfl_xor(s.M, mask, 64), __shfl_xor(s.S, mask, 64), __shfl_xor(s.A, mask, 64)});
-    acc[j] = s;
+      for (int mask = 8; mask <= 32; mask <<= 1)
+        s = softacc_merge(s, SoftAcc{__shfl_xor(s.M, mask, 64), __shfl_xor(s.S, mask, 64), __shfl_xor(s.A, mask, 64)});
+      acc[j] = s;
+    }
+    if (g == 0 && vok) store_entry8<DOUT>(acc, out + ((int64_t)(t.entry_start + e) * c + ch0 + v * 8) * OS);
   }
-  if (g == 0 && vok) store_entry8<DOUT>(acc, out + ((int64_t)(t.entry_start + e) * c + ch0 + v * 8) * OS);
 }
 
 }  // namespace
