@@ -95,6 +95,61 @@ def cpu_baseline(case_csa, case_hca, sample_tokens: int):
                       f"{dt:.2f} s; {tokens / dt:.1f} tokens/s"}
 
 
+def indexer_keys(sc, synth, torch, csa, lengths, steps):
+    """The indexer-key compressor: the same fused CSA operator at c^I = 128
+    over the same packed hidden states (its own weights and biases)."""
+    cI = 128
+    d = csa.H.shape[1]
+    ik = synth.compressor_case("csa", lengths, d, cI, 4, seed=1, in_dtype="bf16", bias_std=0.02, device=csa.H.device,
+                               H=csa.H)
+    b = ik.biases
+    call = lambda: sc.compress_fused("csa", ik.H, ik.Wt_cat, b["Ba"], b["Bb"], 4, ik.cu_seqlens, "bf16")
+    call()
+    torch.cuda.synchronize()
+    ev = _events(torch, 2)
+    ev[0].record()
+    for _ in range(steps):
+        call()
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    T = int(ik.H.shape[0])
+    flops = 2.0 * T * d * 4 * cI
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": f"indexer keys: fused CSA m=4, c=128 over the same T={T} tokens, d={d}, bf16 out",
+            "ms": ms, "entries_per_s": ik.n_entries / (ms * 1e-3), "tflops": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS}
+
+
+def decode_append(sc, torch, csa, batches, steps):
+    """Decode-time CSA append: nb sequences each complete one block of 4
+    tokens (rows taken from the packed hidden states); the b-stream state is
+    carried in place."""
+    d = csa.H.shape[1]
+    c = csa.c
+    b = csa.biases
+    res = {}
+    for nb in batches:
+        H = csa.H[: 4 * nb]
+        state = sc.csa_empty_state(nb, c, H.device)
+        call = lambda: sc.csa_append(H, csa.Wt_cat, b["Ba"], b["Bb"], state, "bf16", state_out=state)
+        call()
+        torch.cuda.synchronize()
+        ev = _events(torch, 2)
+        ev[0].record()
+        for _ in range(steps):
+            call()
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / steps
+        flops = 2.0 * 4 * nb * d * 4 * c
+        wbytes = 4 * c * d * 2 + 4 * nb * d * 2          # weights + new hidden rows
+        res[f"nb={nb}"] = {"us": ms * 1e3, "entries_per_s": nb / (ms * 1e-3),
+                           "mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                           "hbm_frac": wbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    return {"workload": f"CSA decode append, m=4, d={d}, c={c}: one new block per sequence, bf16 out, "
+                        "state updated in place", "batches": res}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -104,6 +159,8 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=262144)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-pool", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the indexer-key compressor and decode-append measurements")
     ap.add_argument("--profile-copy", action="store_true",
                     help="first run a plain 1 GiB device copy (torch copy kernel): the known-size reference that "
                          "scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -217,6 +274,10 @@ def main():
         }
         del pc, st
         torch.cuda.empty_cache()
+
+    if not args.no_extras:
+        out["indexer_keys"] = indexer_keys(sc, synth, torch, csa, lengths, args.steps)
+        out["decode_append"] = decode_append(sc, torch, csa, (64, 1024, 4096), args.steps)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(csa, hca, args.cpu_sample_tokens)

@@ -164,6 +164,39 @@ int seqcomp_compress_fused(int mode, int64_t m, const void* H, int64_t d, int in
                            void* out, int out_dtype, float* out_scale,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * CSA decode append: the compressor of eq. attn-seqcomp-csa-proj,
+ * -csa-softmax and -csa-pool applied to one new block per sequence, with the
+ * overlapping b-stream carried between calls as a softmax partial.  Each of
+ * nb sequences has just completed a block of m = 4 tokens; entry j is that
+ * block's compressed entry.  No sequence crosses a block of another.
+ *   H         [4 nb x d] in_dtype: block j = rows [4j, 4j + 4) (oldest first).
+ *   Wt        [4c x d], Ba, Bb [4 x c] fp32: as in seqcomp_compress_fused.
+ *   state_in  [nb][3][c] fp32: for sequence j, the b-stream partial of its
+ *             previous block as three planes (M, S, A) -- running maximum of
+ *             log2(e) (Z^b + B^b), sum of 2^(logit - M), and that sum
+ *             weighted by C^b -- exactly as this call writes it to state_out.
+ *             A sequence's first block passes M = -inf, S = A = 0: its
+ *             missing b rows then get weight 0 (eq. attn-seqcomp-overlap-bound).
+ *             The planes are otherwise opaque to the caller.
+ *   state_out [nb][3][c] fp32: block j's own b-stream partial, the state for
+ *             the sequence's next append.  May be the same pointer as
+ *             state_in (updated in place); must not overlap it otherwise.
+ *   out       [nb x c] of out_dtype; out_scale [nb] fp32 for fp8 output.
+ *   workspace seqcomp_append_workspace_bytes(nb, c, out_dtype) bytes (0
+ *             unless the output is fp8).
+ *   Requires d % 64 == 0, c % 16 == 0.  nb == 0 returns SEQCOMP_OK.
+ * Appending a sequence's blocks one call at a time gives the same entries as
+ * seqcomp_compress_fused over the whole sequence (up to rounding order).
+ */
+int seqcomp_csa_append(const void* H, int64_t nb, int64_t d, int in_dtype, const void* Wt, int64_t c,
+                       const float* Ba, const float* Bb, const float* state_in, float* state_out,
+                       void* out, int out_dtype, float* out_scale,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of seqcomp_csa_append; (size_t)-1 on malformed arguments. */
+size_t seqcomp_append_workspace_bytes(int64_t nb, int64_t c, int out_dtype);
+
 #ifdef __cplusplus
 }
 #endif

@@ -11,6 +11,8 @@ Functions (each returns torch tensors on the inputs' device):
 * ``pool_csa(Ca, Cb, Za, Zb, Ba, Bb, m, cu_seqlens, out_dtype)`` -> (entries, scale|None)
 * ``pool_hca(C, Z, B, m, cu_seqlens, out_dtype)``       -> (entries, scale|None)
 * ``compress_fused(mode, H, Wt, Ba, Bb, m, cu_seqlens, out_dtype)`` -> (entries, scale|None)
+* ``csa_append(H, Wt, Ba, Bb, state, out_dtype, state_out)`` -> (entries, scale|None, state)
+* ``csa_empty_state(nb, c, device)``                   -> the state of sequences with no block yet
 
 ``out_dtype`` is one of "f32", "bf16", "fp8" (OCP E4M3FN codes stored as
 uint8 with one fp32 scale per entry).
@@ -25,8 +27,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["SeqcompError", "project", "pool_csa", "pool_hca", "compress_fused", "num_entries",
-           "workspace_bytes", "version", "lib"]
+__all__ = ["SeqcompError", "project", "pool_csa", "pool_hca", "compress_fused", "csa_append", "csa_empty_state",
+           "num_entries", "workspace_bytes", "version", "lib"]
 
 _DT_CODE = {"f32": _lib.F32, "bf16": _lib.BF16, "fp8": _lib.FP8_E4M3}
 _TORCH_IN = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16}
@@ -191,3 +193,39 @@ def compress_fused(mode: str, H, Wt, Ba, Bb, m: int, cu_seqlens=None, out_dtype:
                                         _DT_CODE[out_dtype], _ptr(scale), _ptr(ws), ws_n, _stream(dev)),
            "seqcomp_compress_fused")
     return out, scale
+
+
+def csa_empty_state(nb: int, c: int, device) -> torch.Tensor:
+    """State [nb, 3, c] fp32 of sequences that have no block yet (M = -inf, S = A = 0)."""
+    st = torch.zeros((nb, 3, c), dtype=torch.float32, device=device)
+    st[:, 0, :] = float("-inf")
+    return st
+
+
+def csa_append(H, Wt, Ba, Bb, state=None, out_dtype: str = "bf16", state_out=None):
+    """CSA decode append: H [4 nb x d] holds one newly completed block of 4
+    tokens per sequence; returns (entries [nb x c], scale [nb] or None,
+    state_out [nb, 3, c]).  `state` is what the previous call returned for
+    these sequences (None: every sequence starts here).  Passing
+    state_out=state updates the state in place."""
+    T, d = H.shape
+    if T % 4 != 0:
+        raise ValueError("H must hold whole blocks of 4 rows")
+    nb = T // 4
+    c = Wt.shape[0] // 4
+    if Wt.shape != (4 * c, d):
+        raise ValueError("Wt must be [4*c x d]")
+    dev = H.device
+    if state is None:
+        state = csa_empty_state(nb, c, dev)
+    if state.shape != (nb, 3, c) or state.dtype != torch.float32 or not state.is_contiguous():
+        raise ValueError(f"state must be a contiguous float32 [{nb}, 3, {c}] tensor")
+    if state_out is None:
+        state_out = torch.empty_like(state)
+    out, scale = _alloc_out(nb, c, out_dtype, dev)
+    ws_n = lib().seqcomp_append_workspace_bytes(nb, c, _DT_CODE[out_dtype])
+    ws = _alloc_ws(ws_n, dev)
+    _check(lib().seqcomp_csa_append(_ptr(H), nb, d, _in_code(H), _ptr(Wt), c, _ptr(Ba), _ptr(Bb), _ptr(state),
+                                    _ptr(state_out), _ptr(out), _DT_CODE[out_dtype], _ptr(scale), _ptr(ws), ws_n,
+                                    _stream(dev)), "seqcomp_csa_append")
+    return out, scale, state_out

@@ -36,6 +36,9 @@ SIGNATURES = {
                                   _i64p, _vp, _c_i64, _vp, _c_int, _vp, _vp, _size, _vp]),
     "seqcomp_compress_fused": (_c_int, [_c_int, _c_i64, _vp, _c_i64, _c_int, _vp, _c_i64, _vp, _vp,
                                         _i64p, _vp, _c_i64, _vp, _c_int, _vp, _vp, _size, _vp]),
+    "seqcomp_csa_append": (_c_int, [_vp, _c_i64, _c_i64, _c_int, _vp, _c_i64, _vp, _vp, _vp, _vp,
+                                    _vp, _c_int, _vp, _vp, _size, _vp]),
+    "seqcomp_append_workspace_bytes": (_size, [_c_i64, _c_i64, _c_int]),
 }
 
 _lib = None

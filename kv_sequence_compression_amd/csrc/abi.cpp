@@ -340,4 +340,55 @@ int seqcomp_compress_fused(int mode, int64_t m, const void* H, int64_t d, int in
   return hip_status(e);
 }
 
+size_t seqcomp_append_workspace_bytes(int64_t nb, int64_t c, int out_dtype) {
+  if (nb < 0 || c < 1 || !valid_out_dtype(out_dtype)) return (size_t)-1;
+  if (nb == 0 || out_dtype != SEQCOMP_FP8_E4M3) return 0;
+  return round_up((size_t)nb * c * 4, 256);
+}
+
+int seqcomp_csa_append(const void* H, int64_t nb, int64_t d, int in_dtype, const void* Wt, int64_t c,
+                       const float* Ba, const float* Bb, const float* state_in, float* state_out, void* out,
+                       int out_dtype, float* out_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_in_dtype(in_dtype)) return SEQCOMP_E_DTYPE;
+  if (!valid_out_dtype(out_dtype)) return SEQCOMP_E_DTYPE;
+  if (nb < 0 || nb * 4 > kMaxRows) return SEQCOMP_E_SHAPE;
+  if (d < 64 || d % 64 != 0 || d > (int64_t(1) << 24)) return SEQCOMP_E_UNSUPPORTED;
+  if (c < 16 || c % 16 != 0 || c > (int64_t(1) << 20)) return SEQCOMP_E_UNSUPPORTED;
+  // the kernels address one 256-row tile of H and all of Wt with 32-bit byte offsets
+  if (4 * c * d * elt_size(in_dtype) >= (int64_t(1) << 32) || 256 * d * elt_size(in_dtype) >= (int64_t(1) << 32))
+    return SEQCOMP_E_UNSUPPORTED;
+  int st;
+  Range out_r, scale_r;
+  if ((st = check_output(out_dtype, out, out_scale, nb, c, &out_r, &scale_r))) return st;
+  if (nb == 0) return SEQCOMP_OK;
+  if (!H || !Wt || !Ba || !Bb || !state_in || !state_out) return SEQCOMP_E_NULL;
+  if (!aligned16(H) || !aligned16(Wt) || !aligned16(Ba) || !aligned16(Bb) || !aligned16(state_in) ||
+      !aligned16(state_out))
+    return SEQCOMP_E_ALIGN;
+  const size_t need = seqcomp_append_workspace_bytes(nb, c, out_dtype);
+  Range ws_r;
+  if ((st = check_workspace(workspace, workspace_bytes, need, &ws_r))) return st;
+  const int es = elt_size(in_dtype);
+  const size_t state_bytes = (size_t)nb * 3 * c * 4;
+  Range reads[5];
+  int nr = 0;
+  reads[nr++] = range_of(H, (size_t)nb * 4 * d * es);
+  reads[nr++] = range_of(Wt, (size_t)4 * c * d * es);
+  reads[nr++] = range_of(Ba, (size_t)4 * c * 4);
+  reads[nr++] = range_of(Bb, (size_t)4 * c * 4);
+  // the state may be updated in place (same pointer); any other overlap is an error
+  if (state_in != state_out) reads[nr++] = range_of(state_in, state_bytes);
+  const Range writes[4] = {out_r, scale_r, ws_r, range_of(state_out, state_bytes)};
+  if ((st = check_alias(writes, 4, reads, nr))) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool fp8 = out_dtype == SEQCOMP_FP8_E4M3;
+  void* dst = fp8 ? workspace : out;
+  const int dst_dt = fp8 ? DT_F32 : out_dtype;
+  hipError_t e = launch_csa_append(in_dtype, dst_dt, H, nb, (int)d, Wt, (int)c, Ba, Bb, state_in, state_out, dst, s);
+  if (e == hipSuccess && fp8)
+    e = launch_quant_fp8(reinterpret_cast<const float*>(dst), nb, (int)c, static_cast<uint8_t*>(out), out_scale, s);
+  return hip_status(e);
+}
+
 }  // extern "C"

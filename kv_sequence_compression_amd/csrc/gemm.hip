@@ -54,7 +54,7 @@ constexpr int kLdsB = kStagesA * kSlabBytes;    // offset of the Wt slots
 constexpr int kLdsBytes = (kStagesA + kStagesB) * kSlabBytes;   // 160 KiB: all of a CU's LDS
 constexpr int kLoadsPerSlab = kTile / 4 / 8;    // global_load_lds per wave and operand slab (8 rows each)
 
-enum : int { MODE_PROJECT = 0, MODE_CSA = 1, MODE_HCA = 2 };
+enum : int { MODE_PROJECT = 0, MODE_CSA = 1, MODE_HCA = 2, MODE_CSA_APPEND = 3 };
 
 // Slot of 16-byte chunk kc (0..7) in 128-byte tile row r: kc ^ f(r) with
 // f(r) = (r ^ (r >> 3)) & 7.  A fragment read takes one chunk of 32
@@ -90,6 +90,10 @@ struct Args {
   const TileRec* tiles;
   float* halo;
   char* out;
+  // CSA append: state of every block's previous block (b-stream partial)
+  const float* state_in;   // [nb][3][c]: M, S, A planes
+  float* state_out;        // [nb][3][c]
+  int64_t nb;              // blocks (= entries)
   // grid
   int n_mt, n_nt;
 };
@@ -401,7 +405,7 @@ template <int MODE>
 __device__ __forceinline__ int b_row_of(int n, int nt, int c, int n_out) {
   if (MODE == MODE_PROJECT) return min(nt * kTile + n, n_out - 1);
   const int half = n >> 7;                 // which wave column
-  if (MODE == MODE_CSA) {                  // 4 streams x 32 channels per wave column
+  if (MODE == MODE_CSA || MODE == MODE_CSA_APPEND) {   // 4 streams x 32 channels per wave column
     const int s = (n & 127) >> 5, j = n & 31;
     const int ch = nt * 64 + half * 32 + j;
     return s * c + min(ch, c - 1);
@@ -585,6 +589,52 @@ __device__ void epilogue_csa(const Args& a, WaveAcc& acc, const TileRec& t, int 
   }
 }
 
+// CSA append epilogue (decode): the tile's rows are 64 independent blocks of
+// m = 4 tokens, block j being the newest block of its own sequence.  Its
+// entry merges the block's a-partial with the b-partial of the sequence's
+// previous block, which the caller carries from the previous append in
+// state_in (M = -inf, S = A = 0 for a sequence's first block: the entry-0
+// rule of eq. attn-seqcomp-overlap-bound); the block's own b-partial becomes
+// the state for its successor.  Same accumulator layout as epilogue_csa: run
+// q of lane half h is block 32 wm + 8 ms + 2 q + h of the tile.
+template <int DOUT>
+__device__ void epilogue_csa_append(const Args& a, WaveAcc& acc, int mt, int nt, int lane, int wm, int wn,
+                                    const float (&ba)[4], const float (&bb)[4]) {
+  const int col = lane & 31, h = lane >> 5;
+  const int c = a.c;
+  const int ch = nt * 64 + wn * 32 + col;
+  const bool ok = ch < c;
+  const int64_t j0 = (int64_t)mt * 64;
+  // the 16 previous-block partials this lane merges, loaded up front
+  SoftAcc prev[16];
+#pragma unroll
+  for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t j = min(j0 + wm * 32 + ms * 8 + q * 2 + h, a.nb - 1);
+      const float* st = a.state_in + j * 3 * c + min(ch, c - 1);
+      prev[ms * 4 + q] = SoftAcc{st[0], st[c], st[2 * c]};
+    }
+#pragma unroll
+  for (int ms = 0; ms < 4; ++ms) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const SoftAcc pa = partial4(acc[ms][2], acc[ms][0], q, ba);
+      const SoftAcc pb = partial4(acc[ms][3], acc[ms][1], q, bb);
+      const int64_t j = j0 + wm * 32 + ms * 8 + q * 2 + h;
+      const SoftAcc m = softacc_merge(pa, prev[ms * 4 + q]);
+      if (ok && j < a.nb) {
+        store1<DOUT>(a.out, j * c + ch, m.A / m.S);
+        float* so = a.state_out + j * 3 * c + ch;
+        so[0] = pb.M;
+        so[c] = pb.S;
+        so[2 * c] = pb.A;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // HCA epilogue (m' = 128): wave row wm is block wm of the tile; accumulator
 // [ms][qq] holds C and [ms][2 + qq] holds Z at channel 128 nt + 64 wn + 32 qq + col.
 // The tile's bias slice B[0:128][128 nt : 128 nt + 128] is first staged in
@@ -654,7 +704,7 @@ __device__ __forceinline__ void run_tile(const Args& a, int L, char* lds) {
   int64_t row0;
   int nvalid;
   TileRec t{};
-  if (MODE == MODE_PROJECT) {
+  if (MODE == MODE_PROJECT || MODE == MODE_CSA_APPEND) {
     row0 = (int64_t)mt * kTile;
     nvalid = (int)min<int64_t>(kTile, a.T - row0);
   } else {
@@ -674,11 +724,12 @@ __device__ __forceinline__ void run_tile(const Args& a, int L, char* lds) {
     b_off[i] = (uint32_t)((int64_t)b_row_of<MODE>(r, nt, a.c, a.n_out) * a.lda + kc * 16);
   }
   float ba[4] = {0.f, 0.f, 0.f, 0.f}, bb[4] = {0.f, 0.f, 0.f, 0.f};
-  if (MODE == MODE_CSA) csa_bias(a, nt, lane, wn, ba, bb);
+  if (MODE == MODE_CSA || MODE == MODE_CSA_APPEND) csa_bias(a, nt, lane, wn, ba, bb);
   WaveAcc acc;
   mainloop<DIN>(a_base, a_off, a.Wt, b_off, a.nk, lds, w, lane, wm, wn, acc);
   if (MODE == MODE_PROJECT) epilogue_project<DOUT>(a, acc, mt, nt, lane, wm, wn);
   else if (MODE == MODE_CSA) epilogue_csa<DOUT>(a, acc, t, mt, nt, lane, wm, wn, lds, ba, bb);
+  else if (MODE == MODE_CSA_APPEND) epilogue_csa_append<DOUT>(a, acc, mt, nt, lane, wm, wn, ba, bb);
   else epilogue_hca<DOUT>(a, acc, t, nt, tid, wm, wn, lds);
 }
 
@@ -793,6 +844,29 @@ hipError_t launch_fused(int mode, int in_dt, int out_dt, const void* H, int d, c
   }
   a.n_nt = (c + 127) / 128;   // HCA: 128 channels x 2 streams per N tile
   return dispatch<MODE_HCA>(in_dt, out_dt, a, stream);
+}
+
+hipError_t launch_csa_append(int in_dt, int out_dt, const void* H, int64_t nb, int d, const void* Wt, int c,
+                             const float* Ba, const float* Bb, const float* state_in, float* state_out, void* out,
+                             hipStream_t stream) {
+  Args a{};
+  const int es = in_dt == DT_BF16 ? 2 : 4;
+  a.H = static_cast<const char*>(H);
+  a.Wt = static_cast<const char*>(Wt);
+  a.lda = (int64_t)d * es;
+  a.nk = d * es / kRowBytes;
+  a.T = nb * 4;
+  a.c = c;
+  a.Ba = Ba;
+  a.Bb = Bb;
+  a.out = static_cast<char*>(out);
+  a.state_in = state_in;
+  a.state_out = state_out;
+  a.nb = nb;
+  a.n_out = 1;
+  a.n_mt = (int)((a.T + kTile - 1) / kTile);
+  a.n_nt = (c + 63) / 64;
+  return dispatch<MODE_CSA_APPEND>(in_dt, out_dt, a, stream);
 }
 
 hipError_t launch_csa_fixup(int out_dt, const TileRec* tiles, int n_tiles, int c, const float* halo, void* out,

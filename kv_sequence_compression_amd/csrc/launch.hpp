@@ -52,6 +52,13 @@ hipError_t launch_fused(int mode, int in_dt, int out_dt, const void* H, int d, c
                         const float* Ba, const float* Bb, const TileRec* tiles, int n_tiles, void* out,
                         float* halo, hipStream_t stream);
 
+// CSA decode append: nb independent blocks of 4 rows of H; entry j merges
+// block j's a-partial with state_in[j] (the previous block's b-partial, fp32
+// [nb][3][c]) and block j's b-partial goes to state_out[j].
+hipError_t launch_csa_append(int in_dt, int out_dt, const void* H, int64_t nb, int d, const void* Wt, int c,
+                             const float* Ba, const float* Bb, const float* state_in, float* state_out, void* out,
+                             hipStream_t stream);
+
 hipError_t launch_csa_fixup(int out_dt, const TileRec* tiles, int n_tiles, int c, const float* halo,
                             void* out, hipStream_t stream);
 

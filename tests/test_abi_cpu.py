@@ -166,3 +166,47 @@ def test_project_rejects_bad_arguments(lib):
     assert fused(lib, d=1 << 22, c=16, in_dt=_lib.F32) == S["SEQCOMP_E_UNSUPPORTED"]
     # ... and a 256-row tile of Y too
     assert f(A, 64, 64, _lib.BF16, B_, 16, OUT, 1 << 22, _lib.BF16, None) == S["SEQCOMP_E_UNSUPPORTED"]
+
+
+STATE, STATE2 = 0x90000000, 0x98000000
+
+
+def append(lib, **kw):
+    a = dict(H=A, nb=100, d=7168, in_dt=_lib.BF16, Wt=B_, c=512, Ba=BIAS, Bb=BIAS2, st_in=STATE, st_out=STATE2,
+             out=OUT, out_dt=_lib.BF16, scale=0, ws=0, ws_bytes=0)
+    a.update(kw)
+    return lib.seqcomp_csa_append(a["H"], a["nb"], a["d"], a["in_dt"], a["Wt"], a["c"], a["Ba"], a["Bb"],
+                                  a["st_in"], a["st_out"], a["out"], a["out_dt"], a["scale"], a["ws"], a["ws_bytes"],
+                                  None)
+
+
+def test_append_workspace(lib):
+    f = lib.seqcomp_append_workspace_bytes
+    assert f(100, 512, _lib.BF16) == 0 and f(0, 512, _lib.FP8_E4M3) == 0
+    assert f(100, 512, _lib.FP8_E4M3) == 100 * 512 * 4
+    assert f(-1, 512, _lib.BF16) == ctypes.c_size_t(-1).value
+    assert f(1, 512, 9) == ctypes.c_size_t(-1).value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(in_dt=_lib.FP8_E4M3), "SEQCOMP_E_DTYPE"),
+    (dict(out_dt=5), "SEQCOMP_E_DTYPE"),
+    (dict(nb=-1), "SEQCOMP_E_SHAPE"),
+    (dict(nb=1 << 30), "SEQCOMP_E_SHAPE"),
+    (dict(d=7200), "SEQCOMP_E_UNSUPPORTED"),
+    (dict(c=100), "SEQCOMP_E_UNSUPPORTED"),
+    (dict(d=1 << 22, c=16, in_dt=_lib.F32), "SEQCOMP_E_UNSUPPORTED"),
+    (dict(H=0), "SEQCOMP_E_NULL"),
+    (dict(st_in=0), "SEQCOMP_E_NULL"),
+    (dict(st_out=0), "SEQCOMP_E_NULL"),
+    (dict(out=0), "SEQCOMP_E_NULL"),
+    (dict(out_dt=_lib.FP8_E4M3, scale=0, ws=WS, ws_bytes=1 << 20), "SEQCOMP_E_NULL"),
+    (dict(out_dt=_lib.FP8_E4M3, scale=SCALE), "SEQCOMP_E_WORKSPACE"),
+    (dict(st_in=STATE + 4), "SEQCOMP_E_ALIGN"),
+    (dict(st_out=STATE + 16), "SEQCOMP_E_ALIAS"),          # partial overlap with the input state
+    (dict(st_out=A + 4096), "SEQCOMP_E_ALIAS"),            # the new state over H
+    (dict(out=STATE2 + 64), "SEQCOMP_E_ALIAS"),            # entries over the new state
+    (dict(nb=0, H=0, out=0, st_in=0, st_out=0), "SEQCOMP_OK"),
+])
+def test_append_rejects_bad_arguments(lib, kw, code):
+    assert append(lib, **kw) == S[code]
