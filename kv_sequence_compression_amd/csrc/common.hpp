@@ -73,12 +73,17 @@ __device__ __forceinline__ void softacc_init(SoftAcc& s) {
 
 // Merge two partial accumulators (exact up to rounding: rescale both to the
 // larger maximum).  Either side may be empty (M = -inf, S = A = 0).
+// One exponential: the side with the larger maximum keeps factor 1 (what
+// 2^(M - M) gives exactly), the other gets 2^-|x.M - y.M|.
 __device__ __forceinline__ SoftAcc softacc_merge(SoftAcc x, SoftAcc y) {
 #pragma clang fp contract(off)
   const float M = fmaxf(x.M, y.M);
   if (M == -INFINITY) return x;
-  const float fx = exp2_hw(x.M - M);
-  const float fy = exp2_hw(y.M - M);
+  const float dm = x.M - y.M;                       // +-inf when one side is empty
+  const float e = exp2_hw(-fabsf(dm));
+  const bool x_top = dm >= 0.f;
+  const float fx = x_top ? 1.f : e;
+  const float fy = x_top ? e : 1.f;
   SoftAcc r;
   r.M = M;
   r.S = x.S * fx + y.S * fy;

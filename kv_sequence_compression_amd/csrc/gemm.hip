@@ -439,20 +439,17 @@ __device__ __forceinline__ SoftAcc partial4(const f32x16_t& z, const f32x16_t& v
   return s;
 }
 
-__device__ __forceinline__ SoftAcc shfl_acc(const SoftAcc& s, int src) {
-  SoftAcc r;
-  r.M = __shfl(s.M, src, 64);
-  r.S = __shfl(s.S, src, 64);
-  r.A = __shfl(s.A, src, 64);
-  return r;
+// The partial of lane l ^ 32 (the other lane half, same column), through the
+// gfx950 half-swap: v_permlane32_swap(v, v) leaves lanes 0..31 of its second
+// result holding v of lanes 32..63 and lanes 32..63 of its first result
+// holding v of lanes 0..31 -- no LDS round trip.
+__device__ __forceinline__ float xor32(float v, bool upper) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(upper ? r[0] : r[1]);
 }
 
-__device__ __forceinline__ SoftAcc shfl_xor_acc(const SoftAcc& s, int mask) {
-  SoftAcc r;
-  r.M = __shfl_xor(s.M, mask, 64);
-  r.S = __shfl_xor(s.S, mask, 64);
-  r.A = __shfl_xor(s.A, mask, 64);
-  return r;
+__device__ __forceinline__ SoftAcc xor32_acc(const SoftAcc& s, bool upper) {
+  return SoftAcc{xor32(s.M, upper), xor32(s.S, upper), xor32(s.A, upper)};
 }
 
 template <int DOUT>
@@ -561,7 +558,7 @@ __device__ void epilogue_csa(const Args& a, WaveAcc& acc, const TileRec& t, int 
       // Lane l ^ 32 holds the other half of this run pair: for h = 1 it is
       // the previous block (h = 0, same q); for h = 0 it is run (q, h = 1),
       // the previous block of run (q + 1, h = 0) -- carried to the next step.
-      const SoftAcc px = shfl_xor_acc(pb, 32);
+      const SoftAcc px = xor32_acc(pb, h != 0);
       const SoftAcc prev = h ? px : carry;
       carry = px;
       const int blk = wm * 32 + ms * 8 + q * 2 + h;  // block (= entry) index inside the tile
@@ -684,7 +681,7 @@ __device__ void epilogue_hca(const Args& a, WaveAcc& acc, const TileRec& t, int 
         s = softacc_merge(s, partial4(acc[ms][2 + qq], acc[ms][qq], q, b));
       }
     }
-    s = softacc_merge(s, shfl_xor_acc(s, 32));
+    s = softacc_merge(s, xor32_acc(s, h != 0));
     if (ok && block_ok && h == 0) store1<DOUT>(a.out, ((int64_t)t.entry_start + wm) * c + ch, s.A / s.S);
   }
 }
