@@ -188,7 +188,7 @@ int pool_common(bool csa, const void* const* streams, int n_streams, int64_t ld_
   const int op = csa ? SEQCOMP_OP_POOL_CSA : SEQCOMP_OP_POOL_HCA;
   const WsLayout L = ws_layout(op, 0, m, c, cu_host, batch, out_dtype);
   // one workgroup per (tile, channel slice of 512 / 64 channels) on a 32-bit grid
-  if (L.n_tiles * (csa ? 1 : (c + 63) / 64) >= (int64_t(1) << 31)) return SEQCOMP_E_UNSUPPORTED;
+  if ((L.n_tiles + 7) / 8 * 8 * (csa ? 1 : (c + 63) / 64) >= (int64_t(1) << 31)) return SEQCOMP_E_UNSUPPORTED;
   Range ws_r;
   if ((st = check_workspace(ws, ws_bytes, L.total, &ws_r))) return st;
   Range reads[7];

@@ -97,10 +97,11 @@ __device__ __forceinline__ void stage_bias(lds_f32* dst, const float* __restrict
 // were loaded from a valid row (finite values) and get logit -inf, hence
 // weight exactly 0, so the code has no branches.  Two passes over the rows
 // (maximum, then exponentials and sums) recompute the logit from the raw
-// 16-byte loads and the LDS bias instead of keeping 64 logits live.  (A
-// separate unmasked path for full chunks raises the register count past the
-// 3-waves-per-SIMD limit and measured slower.)
-template <int DIN>
+// 16-byte loads and the LDS bias instead of keeping 64 logits live.
+// MASKED = false drops the per-element selects for kernels whose chunks are
+// always full (HCA with m' % 64 == 0); a runtime choice between the two in
+// one kernel raised the register count past 3 waves per SIMD and was slower.
+template <int DIN, bool MASKED = true>
 __device__ __forceinline__ void fold_chunk(SoftAcc (&acc)[8], const Raw8<DIN> (&z)[8], const Raw8<DIN> (&v)[8],
                                            const lds_f32* const (&bias)[8], uint32_t valid) {
   // No FMA contraction of the sums: the normaliser S and the numerator A take
@@ -111,7 +112,7 @@ __device__ __forceinline__ void fold_chunk(SoftAcc (&acc)[8], const Raw8<DIN> (&
   for (int j = 0; j < 8; ++j) top[j] = acc[j].M;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const bool ok = (valid >> k) & 1u;
+    const bool ok = !MASKED || ((valid >> k) & 1u);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float l = fmaf(raw_get<DIN>(z[k], j), kLog2e, bias[k][j]);
@@ -127,7 +128,7 @@ __device__ __forceinline__ void fold_chunk(SoftAcc (&acc)[8], const Raw8<DIN> (&
   }
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const bool ok = (valid >> k) & 1u;
+    const bool ok = !MASKED || ((valid >> k) & 1u);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float l = fmaf(raw_get<DIN>(z[k], j), kLog2e, bias[k][j]);
@@ -208,19 +209,25 @@ __global__ __launch_bounds__(kPoolThreads) void pool_csa_kernel(
 // w, w + 4, ... of the tile (the bias slice is staged once for all of them).  Lane = 8 g + v: vector v (8 channels) of the slice and row
 // group g, which folds rows g, g + 8, g + 16, ... (so one load instruction
 // reads 8 consecutive rows); three butterfly merges combine the row groups.
-template <int DIN, int DOUT>
+template <int DIN, int DOUT, bool FULL>
 __global__ __launch_bounds__(kPoolThreads) void pool_hca_kernel(
     const char* __restrict__ C, const char* __restrict__ Z, int64_t ld_bytes, const float* __restrict__ B, int m,
-    int c, const TileRec* __restrict__ tiles, char* __restrict__ out) {
+    int c, const TileRec* __restrict__ tiles, int n_tiles, char* __restrict__ out) {
   constexpr int ES = DTypeSize<DIN>::value;
   constexpr int OS = DTypeSize<DOUT>::value;
   extern __shared__ float sB_[];                  // [m][width]: log2e * B slice
   lds_f32* sB = (lds_f32*)sB_;
-  // 1-D grid, slice fastest: the slices of one tile are dispatched together
+  // 1-D grid.  The hardware hands workgroup w to XCD w mod 8; XCD x takes
+  // tiles x, x + 8, x + 16, ... and all channel slices of a tile one after
+  // the other, so the slices of a row are read by one XCD close in time
+  // (measured: 63% -> 69% of HBM peak against the slices of a tile spread
+  // over all eight XCDs).
   const int n_slices = (c + kHcaSlice - 1) / kHcaSlice;
-  const int tile = blockIdx.x / n_slices;
+  const int xw = blockIdx.x & 7, kw = blockIdx.x >> 3;
+  const int tile = xw + 8 * (kw / n_slices);
+  if (tile >= n_tiles) return;                    // the grid is padded to 8 tiles
   const TileRec t = tiles[tile];
-  const int ch0 = (blockIdx.x - tile * n_slices) * kHcaSlice;
+  const int ch0 = (kw % n_slices) * kHcaSlice;
   const int width = min(kHcaSlice, c - ch0);
   stage_bias(sB, B, m, c, ch0, width);
   __syncthreads();
@@ -251,7 +258,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_hca_kernel(
         ld_raw<DIN>(x[k], C + row * ld_bytes + col);
         bias[k] = &sB[rr * width + vv * 8];
       }
-      fold_chunk<DIN>(acc, z, x, bias, valid);
+      fold_chunk<DIN, !FULL>(acc, z, x, bias, valid);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -287,16 +294,23 @@ hipError_t launch_pool_csa(int in_dt, int out_dt, const void* Ca, const void* Cb
 hipError_t launch_pool_hca(int in_dt, int out_dt, const void* C, const void* Z, int64_t ld_in, const float* B,
                            int m, int c, const TileRec* tiles, int n_tiles, void* out, hipStream_t stream) {
   const int64_t ldb = ld_in * (in_dt == DT_BF16 ? 2 : 4);
-  const dim3 grid((unsigned)((int64_t)n_tiles * ((c + kHcaSlice - 1) / kHcaSlice))), block(kPoolThreads);
+  const dim3 grid((unsigned)((int64_t)(n_tiles + 7) / 8 * 8 * ((c + kHcaSlice - 1) / kHcaSlice))),
+      block(kPoolThreads);
   const size_t lds = (size_t)m * min(c, kHcaSlice) * sizeof(float);      // <= 64 KiB for m <= 256
   auto args = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, block, lds, stream, (const char*)C, (const char*)Z, ldb, B, m, c, tiles,
-                       (char*)out);
+                       n_tiles, (char*)out);
   };
-  if (in_dt == DT_BF16 && out_dt == DT_BF16) args(pool_hca_kernel<DT_BF16, DT_BF16>);
-  else if (in_dt == DT_BF16 && out_dt == DT_F32) args(pool_hca_kernel<DT_BF16, DT_F32>);
-  else if (in_dt == DT_F32 && out_dt == DT_BF16) args(pool_hca_kernel<DT_F32, DT_BF16>);
-  else args(pool_hca_kernel<DT_F32, DT_F32>);
+  // every fold step of a lane is 8 valid rows when m is a multiple of 64
+  const bool full = m % 64 == 0;
+  if (in_dt == DT_BF16 && out_dt == DT_BF16)
+    full ? args(pool_hca_kernel<DT_BF16, DT_BF16, true>) : args(pool_hca_kernel<DT_BF16, DT_BF16, false>);
+  else if (in_dt == DT_BF16 && out_dt == DT_F32)
+    full ? args(pool_hca_kernel<DT_BF16, DT_F32, true>) : args(pool_hca_kernel<DT_BF16, DT_F32, false>);
+  else if (in_dt == DT_F32 && out_dt == DT_BF16)
+    full ? args(pool_hca_kernel<DT_F32, DT_BF16, true>) : args(pool_hca_kernel<DT_F32, DT_BF16, false>);
+  else
+    full ? args(pool_hca_kernel<DT_F32, DT_F32, true>) : args(pool_hca_kernel<DT_F32, DT_F32, false>);
   return hipGetLastError();
 }
 
