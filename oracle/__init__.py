@@ -13,7 +13,10 @@ Sources (web pages, cited by title and equation/table label):
   table tbl-attn-seqcomp-overlap.
 * "Ch 04 · CSA — 长上下文的快通道" -- section 3 (token-level compressor,
   the 12-token worked example).
-* "Ch 05 · HCA — 长上下文的全景镜" -- section 2 (HCA compression formula).
+* "Ch 05 · HCA — 长上下文的全景镜" -- section 2 (HCA compression formula) and
+  the section on partial RoPE.
+* "混合压缩注意力双方案解析：CSA与HCA技术对比与选型指南" -- section 3
+  (mixed-precision storage).
 
 Every function is pinned by ``tests/test_oracle_pins.py`` against facts that
 do not come from the oracle itself (exact rational arithmetic, closed forms,
@@ -39,4 +42,9 @@ from .encode import (  # noqa: F401
     fp8_e4m3_encode,
     fp8_entry_quantize,
     FP8_E4M3_MAX,
+)
+from .rope_store import (  # noqa: F401
+    entry_positions,
+    rope_partial,
+    rope_mixed_store,
 )
