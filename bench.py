@@ -150,6 +150,32 @@ def decode_append(sc, torch, csa, batches, steps):
                         "state updated in place", "batches": res}
 
 
+def rope_store(sc, torch, csa, steps):
+    """Partial RoPE (last 64 dims) + bf16/fp8 mixed store of the fp32 CSA
+    entries of the batch into a cache, one row per entry."""
+    b = csa.biases
+    ent, _ = sc.compress_fused("csa", csa.H, csa.Wt_cat, b["Ba"], b["Bb"], 4, csa.cu_seqlens, "f32")
+    E, c = ent.shape
+    r = 64
+    cache = sc.rope_cache(E, c, r, ent.device)
+    call = lambda: sc.rope_store(ent, 4, csa.cu_seqlens, cache, r)
+    call()
+    torch.cuda.synchronize()
+    ev = _events(torch, 2)
+    ev[0].record()
+    for _ in range(steps):
+        call()
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    nbytes = E * c * 4 + E * ((c - r) + 4 + 2 * r)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del ent, cache
+    torch.cuda.empty_cache()
+    return {"workload": f"RoPE store of the varlen CSA entries: E={E}, c={c}, r={r}, fp32 in, fp8+bf16 out",
+            "us": ms * 1e3, "entries_per_s": E / (ms * 1e-3), "gbs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -278,6 +304,7 @@ def main():
     if not args.no_extras:
         out["indexer_keys"] = indexer_keys(sc, synth, torch, csa, lengths, args.steps)
         out["decode_append"] = decode_append(sc, torch, csa, (64, 1024, 4096), args.steps)
+        out["rope_store"] = rope_store(sc, torch, csa, args.steps)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(csa, hca, args.cpu_sample_tokens)

@@ -197,6 +197,37 @@ int seqcomp_csa_append(const void* H, int64_t nb, int64_t d, int in_dtype, const
 /* Workspace bytes of seqcomp_csa_append; (size_t)-1 on malformed arguments. */
 size_t seqcomp_append_workspace_bytes(int64_t nb, int64_t c, int out_dtype);
 
+/*
+ * Partial RoPE and mixed-precision store of compressed entries into a cache
+ * ("Ch 05 · HCA — 长上下文的全景镜", section on partial RoPE;
+ * "混合压缩注意力双方案解析", section 3 on mixed-precision storage).
+ *   entries   [E x c] of in_dtype (F32 or BF16): the packed output of a
+ *             compressor call over the batch described by cu_seqlens and m
+ *             (E = sum_b floor(L_b / m)).
+ *   Entry e, compressing block i of sequence b, has position
+ *   pos0[b] + m i + (m - 1) / 2 (the block centre; pos0_dev [batch] int64,
+ *   NULL for all zero).  Its last r = rope_dims dimensions are turned in
+ *   adjacent pairs: pair k (columns c - r + 2k, c - r + 2k + 1) by the angle
+ *   pos * rope_base^(-2k / r); the first c - r dimensions are left as they are.
+ *   Entry e goes to cache row slots_dev[e] (int64 [E]; NULL: row e); rows
+ *   must be distinct; a row outside [0, n_slots) is not stored.
+ *   cache_nope  [n_slots x (c - r)] OCP E4M3 codes of the first c - r
+ *               dimensions divided by cache_scale[row];
+ *   cache_scale [n_slots] fp32: max |x| over those c - r dimensions / 448 (1 if
+ *               they are all zero);
+ *   cache_rope  [n_slots x r] bf16 (round to nearest even) of the rotated part.
+ *   Requires c % 16 == 0, 0 <= r <= c, r % 8 == 0, rope_base > 0.
+ *   workspace: seqcomp_rope_store_workspace_bytes(m, cu, batch) bytes.
+ */
+int seqcomp_rope_store(const void* entries, int in_dtype, int64_t c, int64_t m,
+                       const int64_t* cu_seqlens_host, const int64_t* cu_seqlens_dev, int64_t batch,
+                       const int64_t* pos0_dev, int64_t rope_dims, double rope_base,
+                       const int64_t* slots_dev, int64_t n_slots, uint8_t* cache_nope, float* cache_scale,
+                       uint16_t* cache_rope, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of seqcomp_rope_store; (size_t)-1 on malformed arguments. */
+size_t seqcomp_rope_store_workspace_bytes(int64_t m, const int64_t* cu_seqlens_host, int64_t batch);
+
 #ifdef __cplusplus
 }
 #endif

@@ -13,6 +13,7 @@ Functions (each returns torch tensors on the inputs' device):
 * ``compress_fused(mode, H, Wt, Ba, Bb, m, cu_seqlens, out_dtype)`` -> (entries, scale|None)
 * ``csa_append(H, Wt, Ba, Bb, state, out_dtype, state_out)`` -> (entries, scale|None, state)
 * ``csa_empty_state(nb, c, device)``                   -> the state of sequences with no block yet
+* ``rope_store(entries, m, cu_seqlens, cache, ...)``     partial RoPE + bf16/fp8 store into a cache
 
 ``out_dtype`` is one of "f32", "bf16", "fp8" (OCP E4M3FN codes stored as
 uint8 with one fp32 scale per entry).
@@ -28,7 +29,7 @@ import torch
 from . import _lib
 
 __all__ = ["SeqcompError", "project", "pool_csa", "pool_hca", "compress_fused", "csa_append", "csa_empty_state",
-           "num_entries", "workspace_bytes", "version", "lib"]
+           "rope_store", "rope_cache", "num_entries", "workspace_bytes", "version", "lib"]
 
 _DT_CODE = {"f32": _lib.F32, "bf16": _lib.BF16, "fp8": _lib.FP8_E4M3}
 _TORCH_IN = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16}
@@ -229,3 +230,34 @@ def csa_append(H, Wt, Ba, Bb, state=None, out_dtype: str = "bf16", state_out=Non
                                     _ptr(state_out), _ptr(out), _DT_CODE[out_dtype], _ptr(scale), _ptr(ws), ws_n,
                                     _stream(dev)), "seqcomp_csa_append")
     return out, scale, state_out
+
+
+def rope_cache(n_slots: int, c: int, rope_dims: int, device):
+    """An empty mixed-precision entry cache: (nope [n_slots, c - r] uint8 E4M3
+    codes, scale [n_slots] float32, rope [n_slots, r] bfloat16)."""
+    return (torch.zeros((n_slots, c - rope_dims), dtype=torch.uint8, device=device),
+            torch.zeros((n_slots,), dtype=torch.float32, device=device),
+            torch.zeros((n_slots, rope_dims), dtype=torch.bfloat16, device=device))
+
+
+def rope_store(entries, m: int, cu_seqlens, cache, rope_dims: int = 64, rope_base: float = 10000.0,
+               pos0=None, slots=None):
+    """Partial RoPE on the last `rope_dims` dimensions of every packed entry
+    (position: its block centre plus pos0 of its sequence) and the store into
+    `cache` = (nope, scale, rope) at rows `slots` (default: row e for entry e)."""
+    E, c = entries.shape
+    dev = entries.device
+    host, cu_dev = _cu_arrays(cu_seqlens, dev)
+    nope, scale, rope = cache
+    n_slots = scale.shape[0]
+    if nope.shape != (n_slots, c - rope_dims) or rope.shape != (n_slots, rope_dims):
+        raise ValueError("cache shapes do not match c and rope_dims")
+    p0 = None if pos0 is None else torch.as_tensor(pos0, dtype=torch.int64, device=dev).contiguous()
+    sl = None if slots is None else torch.as_tensor(slots, dtype=torch.int64, device=dev).contiguous()
+    ws_n = lib().seqcomp_rope_store_workspace_bytes(int(m), _i64p(host), host.size - 1)
+    ws = _alloc_ws(ws_n, dev)
+    _check(lib().seqcomp_rope_store(_ptr(entries), _in_code(entries), c, int(m), _i64p(host), _ptr(cu_dev),
+                                    host.size - 1, _ptr(p0), int(rope_dims), float(rope_base), _ptr(sl), n_slots,
+                                    _ptr(nope), _ptr(scale), _ptr(rope), _ptr(ws), ws_n, _stream(dev)),
+           "seqcomp_rope_store")
+    return cache

@@ -39,6 +39,9 @@ SIGNATURES = {
     "seqcomp_csa_append": (_c_int, [_vp, _c_i64, _c_i64, _c_int, _vp, _c_i64, _vp, _vp, _vp, _vp,
                                     _vp, _c_int, _vp, _vp, _size, _vp]),
     "seqcomp_append_workspace_bytes": (_size, [_c_i64, _c_i64, _c_int]),
+    "seqcomp_rope_store": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _i64p, _vp, _c_i64, _vp, _c_i64, ctypes.c_double,
+                                    _vp, _c_i64, _vp, _vp, _vp, _vp, _size, _vp]),
+    "seqcomp_rope_store_workspace_bytes": (_size, [_c_i64, _i64p, _c_i64]),
 }
 
 _lib = None

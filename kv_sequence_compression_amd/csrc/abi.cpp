@@ -391,4 +391,57 @@ int seqcomp_csa_append(const void* H, int64_t nb, int64_t d, int in_dtype, const
   return hip_status(e);
 }
 
+size_t seqcomp_rope_store_workspace_bytes(int64_t m, const int64_t* cu_seqlens_host, int64_t batch) {
+  int64_t T;
+  if (m < 1 || m > (int64_t(1) << 20) || check_cu(cu_seqlens_host, batch, &T) != SEQCOMP_OK) return (size_t)-1;
+  if (entries_of(cu_seqlens_host, batch, m) == 0) return 0;
+  return round_up((size_t)count_tiles(cu_seqlens_host, batch, m, m * kRopeTileEntries) * sizeof(TileRec), 256);
+}
+
+int seqcomp_rope_store(const void* entries, int in_dtype, int64_t c, int64_t m, const int64_t* cu_seqlens_host,
+                       const int64_t* cu_seqlens_dev, int64_t batch, const int64_t* pos0_dev, int64_t rope_dims,
+                       double rope_base, const int64_t* slots_dev, int64_t n_slots, uint8_t* cache_nope,
+                       float* cache_scale, uint16_t* cache_rope, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (!valid_in_dtype(in_dtype)) return SEQCOMP_E_DTYPE;
+  if (c < 16 || c % 16 != 0 || c > (int64_t(1) << 20)) return SEQCOMP_E_UNSUPPORTED;
+  if (m < 1 || m > (int64_t(1) << 20)) return SEQCOMP_E_UNSUPPORTED;
+  if (rope_dims < 0 || rope_dims > c || rope_dims % 8 != 0) return SEQCOMP_E_UNSUPPORTED;
+  if (!(rope_base > 0.0) || rope_base > 1e30) return SEQCOMP_E_SHAPE;   // rejects NaN too
+  int64_t T = 0;
+  int st = check_cu(cu_seqlens_host, batch, &T);
+  if (st) return st;
+  const int64_t E = entries_of(cu_seqlens_host, batch, m);
+  if (n_slots < 0 || (!slots_dev && n_slots < E)) return SEQCOMP_E_SHAPE;
+  if (E == 0) return SEQCOMP_OK;
+  const int64_t cn = c - rope_dims;
+  if (!entries || !cu_seqlens_dev || !cache_scale || (cn > 0 && !cache_nope) || (rope_dims > 0 && !cache_rope))
+    return SEQCOMP_E_NULL;
+  if (!aligned16(entries) || !aligned16(cu_seqlens_dev) || !aligned16(cache_scale) ||
+      (cn > 0 && !aligned16(cache_nope)) || (rope_dims > 0 && !aligned16(cache_rope)) ||
+      (pos0_dev && !aligned16(pos0_dev)) || (slots_dev && !aligned16(slots_dev)))
+    return SEQCOMP_E_ALIGN;
+  const size_t need = seqcomp_rope_store_workspace_bytes(m, cu_seqlens_host, batch);
+  Range ws_r;
+  if ((st = check_workspace(workspace, workspace_bytes, need, &ws_r))) return st;
+  Range reads[4];
+  int nr = 0;
+  reads[nr++] = range_of(entries, (size_t)E * c * elt_size(in_dtype));
+  reads[nr++] = range_of(cu_seqlens_dev, (size_t)(batch + 1) * 8);
+  if (pos0_dev) reads[nr++] = range_of(pos0_dev, (size_t)batch * 8);
+  if (slots_dev) reads[nr++] = range_of(slots_dev, (size_t)E * 8);
+  const Range writes[4] = {cn > 0 ? range_of(cache_nope, (size_t)n_slots * cn) : Range(),
+                           range_of(cache_scale, (size_t)n_slots * 4),
+                           rope_dims > 0 ? range_of(cache_rope, (size_t)n_slots * rope_dims * 2) : Range(), ws_r};
+  if ((st = check_alias(writes, 4, reads, nr))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TileRec* tiles = static_cast<TileRec*>(workspace);
+  const int n_tiles = (int)count_tiles(cu_seqlens_host, batch, m, m * kRopeTileEntries);
+  hipError_t e = launch_plan(cu_seqlens_dev, (int)batch, (int)m, (int)(m * kRopeTileEntries), tiles, n_tiles, s);
+  if (e == hipSuccess)
+    e = launch_rope_store(in_dtype, entries, (int)c, (int)m, cu_seqlens_dev, pos0_dev, (int)rope_dims, rope_base,
+                          slots_dev, n_slots, tiles, n_tiles, cache_nope, cache_scale, cache_rope, s);
+  return hip_status(e);
+}
+
 }  // extern "C"

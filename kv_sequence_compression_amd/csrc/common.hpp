@@ -16,6 +16,8 @@ struct TileRec {
 };
 static_assert(sizeof(TileRec) == 16, "tile record is one 16-byte load");
 enum : int32_t { TILE_FIRST = 1 };
+// flags bits 1..31: index of the tile's sequence in the packed batch
+__host__ __device__ inline int tile_seq(int32_t flags) { return (int)((uint32_t)flags >> 1); }
 
 enum DType : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
 

@@ -59,6 +59,14 @@ hipError_t launch_csa_append(int in_dt, int out_dt, const void* H, int64_t nb, i
                              const float* Ba, const float* Bb, const float* state_in, float* state_out, void* out,
                              hipStream_t stream);
 
+// Partial RoPE + mixed store of packed entries [E x c] (tiles of 64 entries
+// from the planner with tile_rows = 64 m).
+constexpr int kRopeTileEntries = 64;
+hipError_t launch_rope_store(int in_dt, const void* entries, int c, int m, const int64_t* cu_dev,
+                             const int64_t* pos0_dev, int r, double rope_base, const int64_t* slots_dev,
+                             int64_t n_slots, const TileRec* tiles, int n_tiles, uint8_t* nope, float* scale,
+                             uint16_t* rope, hipStream_t stream);
+
 hipError_t launch_csa_fixup(int out_dt, const TileRec* tiles, int n_tiles, int c, const float* halo,
                             void* out, hipStream_t stream);
 

@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_tiles_kernel(const int64_t*
       r.row_start = s_row0[lo] + j * tile_rows;
       r.n_rows = min(tile_rows, s_rows[lo] - j * tile_rows);
       r.entry_start = base_ent + ent0 + j * (tile_rows / m);
-      r.flags = j == 0 ? TILE_FIRST : 0;
+      r.flags = (j == 0 ? TILE_FIRST : 0) | ((b0 + lo) << 1);
       const int idx = base_tile + k;
       if (idx < capacity) tiles[idx] = r;
     }

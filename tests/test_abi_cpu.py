@@ -210,3 +210,47 @@ def test_append_workspace(lib):
 ])
 def test_append_rejects_bad_arguments(lib, kw, code):
     assert append(lib, **kw) == S[code]
+
+
+NOPE, SCL, ROPE, SLOTS, POS0 = 0xA0000000, 0xA8000000, 0xB0000000, 0xB8000000, 0xBC000000
+
+
+def rope_store(lib, **kw):
+    a = dict(ent=A, in_dt=_lib.F32, c=512, m=4, cu=_cu(0, 8192), cu_dev=CU_DEV, pos0=0, r=64, base=10000.0,
+             slots=0, n_slots=2048, nope=NOPE, scale=SCL, rope=ROPE, ws=WS, ws_bytes=1 << 20)
+    a.update(kw)
+    cu = a["cu"]
+    return lib.seqcomp_rope_store(a["ent"], a["in_dt"], a["c"], a["m"], _p(cu), a["cu_dev"], cu.size - 1, a["pos0"],
+                                  a["r"], a["base"], a["slots"], a["n_slots"], a["nope"], a["scale"], a["rope"],
+                                  a["ws"], a["ws_bytes"], None)
+
+
+def test_rope_store_workspace(lib):
+    f = lib.seqcomp_rope_store_workspace_bytes
+    assert f(4, _p(_cu(0, 8192)), 1) == 512          # 32 tiles of 64 entries, 16 B each
+    assert f(4, _p(_cu(0, 3)), 1) == 0
+    assert f(0, _p(_cu(0, 8)), 1) == ctypes.c_size_t(-1).value
+    assert f(4, _p(_cu(0, -1)), 1) == ctypes.c_size_t(-1).value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(in_dt=_lib.FP8_E4M3), "SEQCOMP_E_DTYPE"),
+    (dict(c=100), "SEQCOMP_E_UNSUPPORTED"),
+    (dict(m=0), "SEQCOMP_E_UNSUPPORTED"),
+    (dict(r=60), "SEQCOMP_E_UNSUPPORTED"),
+    (dict(r=520), "SEQCOMP_E_UNSUPPORTED"),
+    (dict(base=0.0), "SEQCOMP_E_SHAPE"),
+    (dict(base=float("nan")), "SEQCOMP_E_SHAPE"),
+    (dict(n_slots=100), "SEQCOMP_E_SHAPE"),                 # no slot map: one row per entry needed
+    (dict(cu=_cu(0, -4)), "SEQCOMP_E_SEQLENS"),
+    (dict(ent=0), "SEQCOMP_E_NULL"),
+    (dict(scale=0), "SEQCOMP_E_NULL"),
+    (dict(rope=0), "SEQCOMP_E_NULL"),
+    (dict(nope=NOPE + 8), "SEQCOMP_E_ALIGN"),
+    (dict(ws_bytes=8), "SEQCOMP_E_WORKSPACE"),
+    (dict(nope=A + 64), "SEQCOMP_E_ALIAS"),                 # cache over the entries
+    (dict(slots=SLOTS, rope=SLOTS - 64), "SEQCOMP_E_ALIAS"),
+    (dict(cu=_cu(0, 3), ent=0, nope=0, scale=0, rope=0), "SEQCOMP_OK"),
+])
+def test_rope_store_rejects_bad_arguments(lib, kw, code):
+    assert rope_store(lib, **kw) == S[code]
