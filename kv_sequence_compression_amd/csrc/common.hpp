@@ -41,6 +41,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
+// Four OCP E4M3FN codes packed little-endian in a word: v_cvt_pk_fp8_f32
+// rounds to nearest even into the OCP E4M3FN grid on gfx950 (a sweep of every
+// fp32 magnitude below 512, both signs, gave the same codes as f32_to_e4m3
+// below); clamping to +-448 first gives the saturating encoding.
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+  const auto sat = [](float x) { return fminf(fmaxf(x, -448.0f), 448.0f); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(a), sat(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(c), sat(d), w, true);
+  return (uint32_t)w;
+}
+
 // OCP E4M3FN encoding of a float: saturate |x| to 448 (the largest finite
 // value, 1.75 * 2^8), round to nearest even.  Below 2^-6 the grid is the
 // subnormal step 2^-9, so the code is rint(|x| * 512) (8 is the smallest

@@ -41,8 +41,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_fp8_kernel(const float* _
     uint32_t* orow = reinterpret_cast<uint32_t*>(out + e * c);
     for (int q = lane; q < nq; q += 64) {
       const float4 x = row[q];                 // second read hits the cache
-      orow[q] = f32_to_e4m3(x.x / s) | (f32_to_e4m3(x.y / s) << 8) | (f32_to_e4m3(x.z / s) << 16) |
-                (f32_to_e4m3(x.w / s) << 24);
+      orow[q] = pack_e4m3x4(x.x / s, x.y / s, x.z / s, x.w / s);
     }
     if (lane == 0) scale[e] = s;
   }

@@ -15,9 +15,9 @@
 // rotated ones as bf16 (round to nearest even).
 //
 // Workgroup = one tile of up to 64 entries of one sequence (tile table from
-// the planner); wave w stores entries w, w + 4, ...; lane l handles 8
-// consecutive channels 8 l + 512 j.  The angle is reduced modulo 2 pi in
-// double precision (positions reach 10^6 tokens and more) before sin / cos.
+// the planner); lane l handles 8 consecutive channels.  The fp8 codes are
+// those of x * (1 / s), which can differ by one code from rounding x / s
+// only when x / s lies within an ulp of a rounding midpoint.
 #include "launch.hpp"
 
 namespace seqcomp {
@@ -32,26 +32,115 @@ __device__ __forceinline__ float wave_max_f(float x) {
   return x;
 }
 
+// Angle of pair `kp` at position `pos`, reduced to [-pi, pi] in double
+// precision (positions of 10^6 tokens and more keep their accuracy), then
+// sin / cos in single precision.
+__device__ __forceinline__ void rope_sincos(double pos, double theta, float& sn, float& cs) {
+  const double two_pi = 6.283185307179586476925286766559;
+  double a = pos * theta;
+  a -= two_pi * rint(a / two_pi);
+  sincosf((float)a, &sn, &cs);
+}
+
+// Encode and store one entry chunk (8 channels at ch0) of lane data x; a
+// RoPE chunk turns its 4 pairs by the angles whose cos / sin are given.
+template <int DIN>
+__device__ __forceinline__ void store_chunk(const float (&x)[8], int ch0, int cn, float inv_s, const float (&cs)[4],
+                                            const float (&sn)[4], bool store, int64_t slot, int r,
+                                            uint8_t* __restrict__ nope, uint16_t* __restrict__ rope) {
+  if (ch0 < cn) {
+    uint2 q;
+    q.x = pack_e4m3x4(x[0] * inv_s, x[1] * inv_s, x[2] * inv_s, x[3] * inv_s);
+    q.y = pack_e4m3x4(x[4] * inv_s, x[5] * inv_s, x[6] * inv_s, x[7] * inv_s);
+    if (store) *reinterpret_cast<uint2*>(nope + slot * cn + ch0) = q;
+  } else {
+    float y[8];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      y[2 * p] = x[2 * p] * cs[p] - x[2 * p + 1] * sn[p];
+      y[2 * p + 1] = x[2 * p] * sn[p] + x[2 * p + 1] * cs[p];
+    }
+    if (store)
+      *reinterpret_cast<uint4*>(rope + slot * r + (ch0 - cn)) =
+          make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
+  }
+}
+
+// c <= 512: a lane holds the 8 channels 8 l of G entries at a time, all their
+// loads in flight together; wave w takes entries G w + g, G w + g + 4 G, ...
+// Larger c: one entry at a time, 8 channels 8 l + 512 j per lane, two passes
+// over the row (the second hits the cache).
 template <int DIN>
 __global__ __launch_bounds__(kRopeThreads) void rope_store_kernel(
     const char* __restrict__ entries, int c, int m, const int64_t* __restrict__ cu, const int64_t* __restrict__ pos0,
     int r, double log2_base, const int64_t* __restrict__ slots, int64_t n_slots, const TileRec* __restrict__ tiles,
     uint8_t* __restrict__ nope, float* __restrict__ scale, uint16_t* __restrict__ rope) {
   constexpr int ES = DTypeSize<DIN>::value;
+  constexpr int G = 4;
   const TileRec t = tiles[blockIdx.x];
   const int seq = tile_seq(t.flags);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int ne = t.n_rows / m;
   const int cn = c - r;                                   // position-free dimensions
-  // tokens from the sequence start to the tile's first block, plus the offset
+  // tokens from the sequence start to the tile's first block centre, plus the offset
   const double base_pos = (double)(t.row_start - cu[seq]) + (pos0 ? (double)pos0[seq] : 0.0) + 0.5 * (m - 1);
-  const double two_pi = 6.283185307179586476925286766559;
+  if (c <= 512) {
+    const int ch0 = 8 * lane;
+    const bool active = ch0 < c;
+    const bool rope_lane = active && ch0 >= cn;
+    // the lane's 4 pair frequencies and the turn of one block (m tokens):
+    // consecutive entries of a group follow by one complex multiplication
+    double theta[4];
+    float step_c[4], step_s[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      theta[p] = rope_lane ? exp2(-2.0 * ((ch0 - cn) / 2 + p) / r * log2_base) : 0.0;
+      rope_sincos((double)m, theta[p], step_s[p], step_c[p]);
+    }
+    for (int k0 = G * w; k0 < ne; k0 += 4 * G) {
+      float x[G][8];
+      int64_t slot[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int k = min(k0 + g, ne - 1);                // past the tile end: re-read the last entry, store nothing
+        const int64_t e = (int64_t)t.entry_start + k;
+        slot[g] = slots ? slots[e] : e;
+        if (active) load8<DIN>(entries + (e * c + ch0) * ES, x[g]);
+        else
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[g][j] = 0.f;
+      }
+      float cs[4], sn[4];
+      if (rope_lane)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) rope_sincos(base_pos + (double)k0 * m, theta[p], sn[p], cs[p]);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float amax = 0.f;
+        if (ch0 < cn)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[g][j]));
+        amax = wave_max_f(amax);
+        const float s = amax > 0.f ? amax / 448.0f : 1.0f;
+        const bool store = k0 + g < ne && slot[g] >= 0 && slot[g] < n_slots;   // out-of-range rows are not stored
+        if (store && lane == 0) scale[slot[g]] = s;
+        if (active) store_chunk<DIN>(x[g], ch0, cn, 1.0f / s, cs, sn, store, slot[g], r, nope, rope);
+        if (rope_lane)
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {                   // advance to the next entry: angle + m theta
+            const float c2 = cs[p] * step_c[p] - sn[p] * step_s[p];
+            sn[p] = sn[p] * step_c[p] + cs[p] * step_s[p];
+            cs[p] = c2;
+          }
+      }
+    }
+    return;
+  }
   for (int k = w; k < ne; k += 4) {
     const int64_t e = (int64_t)t.entry_start + k;
     const int64_t slot = slots ? slots[e] : e;
-    const bool store = slot >= 0 && slot < n_slots;       // out-of-range slots are not stored
+    const bool store = slot >= 0 && slot < n_slots;
     const char* row = entries + e * c * ES;
-    // absolute maximum of the position-free part
     float amax = 0.f;
     for (int ch0 = 8 * lane; ch0 < cn; ch0 += 512) {
       float x[8];
@@ -65,33 +154,14 @@ __global__ __launch_bounds__(kRopeThreads) void rope_store_kernel(
     const double pos = base_pos + (double)k * m;
     for (int ch0 = 8 * lane; ch0 < c; ch0 += 512) {
       float x[8];
-      load8<DIN>(row + (int64_t)ch0 * ES, x);           // the amax pass left it in the cache
-      if (ch0 < cn) {
-        uint2 q;
-        q.x = f32_to_e4m3(x[0] / s) | (f32_to_e4m3(x[1] / s) << 8) | (f32_to_e4m3(x[2] / s) << 16) |
-              (f32_to_e4m3(x[3] / s) << 24);
-        q.y = f32_to_e4m3(x[4] / s) | (f32_to_e4m3(x[5] / s) << 8) | (f32_to_e4m3(x[6] / s) << 16) |
-              (f32_to_e4m3(x[7] / s) << 24);
-        if (store) *reinterpret_cast<uint2*>(nope + slot * cn + ch0) = q;
-      } else {
-        float y[8];
+      load8<DIN>(row + (int64_t)ch0 * ES, x);
+      float cs[4], sn[4];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const int kp = (ch0 - cn) / 2 + p;                          // pair index in the RoPE part
-          const double theta = exp2(-2.0 * kp / r * log2_base);
-          double a = pos * theta;
-          a -= two_pi * rint(a / two_pi);
-          double sn, cs;
-          sincos(a, &sn, &cs);
-          const double x0 = x[2 * p], x1 = x[2 * p + 1];
-          y[2 * p] = (float)(x0 * cs - x1 * sn);
-          y[2 * p + 1] = (float)(x0 * sn + x1 * cs);
-        }
-        if (store)
-          *reinterpret_cast<uint4*>(rope + slot * r + (ch0 - cn)) =
-              make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
-                         pack_bf16x2(y[6], y[7]));
+      for (int p = 0; p < 4; ++p) {
+        const double theta = ch0 >= cn ? exp2(-2.0 * ((ch0 - cn) / 2 + p) / r * log2_base) : 0.0;
+        rope_sincos(pos, theta, sn[p], cs[p]);
       }
+      store_chunk<DIN>(x, ch0, cn, 1.0f / s, cs, sn, store, slot, r, nope, rope);
     }
   }
 }
