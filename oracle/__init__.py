@@ -12,7 +12,7 @@ Sources (web pages, cited by title and equation/table label):
   eq. attn-seqcomp-overlap-bound, eq. attn-seqcomp-hca,
   table tbl-attn-seqcomp-overlap.
 * "Ch 04 · CSA — 长上下文的快通道" -- section 3 (token-level compressor,
-  the 12-token worked example).
+  the 12-token worked example) and section 4 (lightning indexer).
 * "Ch 05 · HCA — 长上下文的全景镜" -- section 2 (HCA compression formula) and
   the section on partial RoPE.
 * "混合压缩注意力双方案解析：CSA与HCA技术对比与选型指南" -- section 3
@@ -47,4 +47,8 @@ from .rope_store import (  # noqa: F401
     entry_positions,
     rope_partial,
     rope_mixed_store,
+)
+from .indexer import (  # noqa: F401
+    index_scores,
+    top_k,
 )

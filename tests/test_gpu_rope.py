@@ -96,3 +96,16 @@ def test_fused_then_store_matches_oracle(gpu_device):
     # stored cache against the oracle store of the GPU's own entries, then the entries against the oracle
     _check(cache, np.arange(out.shape[0]), to64(out), oracle.entry_positions(case.cu_seqlens, 4), 64)
     assert np.max(np.abs(to64(out) - ref)) <= 2e-5
+
+
+def test_rope_store_wide_entries(gpu_device):
+    """c > 512 takes the chunked path: 1024 channels, 128 of them rotated."""
+    lengths = [4 * 9, 4 * 70]
+    cu = synth.cu_from_lengths(lengths)
+    c, r = 1024, 128
+    E = int(sum(L // 4 for L in lengths))
+    X = synth.normal((E, c), 1.0, (13, 1), "cpu", "f32").double().numpy()
+    cache = sc.rope_cache(E, c, r, gpu_device)
+    sc.rope_store(torch.from_numpy(X).float().to(gpu_device), 4, cu, cache, r, pos0=[3, 40000])
+    torch.cuda.synchronize()
+    _check(cache, np.arange(E), X, oracle.entry_positions(cu, 4, [3, 40000]), r)
