@@ -228,6 +228,43 @@ int seqcomp_rope_store(const void* entries, int in_dtype, int64_t c, int64_t m,
 /* Workspace bytes of seqcomp_rope_store; (size_t)-1 on malformed arguments. */
 size_t seqcomp_rope_store_workspace_bytes(int64_t m, const int64_t* cu_seqlens_host, int64_t batch);
 
+/*
+ * Lightning indexer ("Ch 04 · CSA — 长上下文的快通道", section 4): index
+ * scores of queries against compressed indexer keys and, per query, the set
+ * of its k best keys:
+ *     I[t, s] = sum_h w[t, h] * ReLU(q[t, h] . K[s])
+ * over the n_h^I = 64 indexer heads of c^I = 128 dimensions.
+ *   q         [T x 64 x 128] bf16: indexer queries, packed by sequence (cu_q).
+ *   w         [T x 64] fp32: head weights.
+ *   keys      [N x 128] bf16: compressed indexer keys, packed by sequence
+ *             (cu_k; e.g. the output of a CSA compressor with c = 128).
+ *   cu_q, cu_k [batch + 1] int64, host and device copies (same values):
+ *             sequence b owns queries [cu_q[b], cu_q[b+1]) and keys
+ *             [cu_k[b], cu_k[b+1]); a query scores only its own sequence's keys.
+ *   n_valid   [T] int32 (device) or NULL: query t sees the first n_valid[t]
+ *             keys of its sequence (clamped to [0, its key count]), e.g. the
+ *             entries whose blocks are complete at its position; NULL: all.
+ *   k         1..1024.
+ *   out_idx   [T x k] int32: the selected keys (index within the sequence),
+ *             the k visible keys of largest score with ties going to the
+ *             smaller index, listed by increasing index; when fewer than k
+ *             keys are visible, all of them, then -1.
+ *   out_score [T x k] fp32 or NULL: the selected keys' scores (-inf after the
+ *             last selected key).
+ * Scores are fp32 (bf16 products, fp32 accumulation); a key whose score is
+ * NaN is never selected.  Requires n_heads == 64, head_dim == 128, bf16
+ * inputs, and fewer than 2^23 keys per sequence.
+ *   workspace: seqcomp_indexer_workspace_bytes(cu_q_host, batch) bytes.
+ */
+int seqcomp_indexer_topk(const void* q, const float* w, const void* keys, int64_t n_heads, int64_t head_dim,
+                         int in_dtype, const int64_t* cu_q_host, const int64_t* cu_q_dev,
+                         const int64_t* cu_k_host, const int64_t* cu_k_dev, int64_t batch,
+                         const int32_t* n_valid, int64_t k, int32_t* out_idx, float* out_score,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of seqcomp_indexer_topk; (size_t)-1 on malformed arguments. */
+size_t seqcomp_indexer_workspace_bytes(const int64_t* cu_q_host, int64_t batch);
+
 #ifdef __cplusplus
 }
 #endif

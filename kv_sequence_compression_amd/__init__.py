@@ -261,3 +261,34 @@ def rope_store(entries, m: int, cu_seqlens, cache, rope_dims: int = 64, rope_bas
                                     _ptr(nope), _ptr(scale), _ptr(rope), _ptr(ws), ws_n, _stream(dev)),
            "seqcomp_rope_store")
     return cache
+
+
+def indexer_topk(q, w, keys, k: int, cu_q=None, cu_k=None, n_valid=None, with_scores: bool = True):
+    """Lightning-indexer selection: for every query t the k keys s of its
+    sequence with the largest I[t, s] = sum_h w[t, h] ReLU(q[t, h] . keys[s]),
+    ties to the smaller index, listed by increasing key index (-1 past the
+    visible keys).  q [T x 64 x 128] bf16, w [T x 64] fp32, keys [N x 128]
+    bf16; cu_q / cu_k pack queries and keys by sequence (default: one
+    sequence); n_valid [T] int32: keys visible to each query (default: all).
+    Returns (idx int32 [T x k], scores fp32 [T x k] or None)."""
+    T = q.shape[0]
+    N = keys.shape[0]
+    dev = q.device
+    if q.dim() != 3 or keys.dim() != 2 or w.shape != (T, q.shape[1]):
+        raise ValueError("q must be [T x H x D], w [T x H], keys [N x D]")
+    hq, cq = _cu_arrays([0, T] if cu_q is None else cu_q, dev)
+    hk, ck = _cu_arrays([0, N] if cu_k is None else cu_k, dev)
+    if hq.size != hk.size:
+        raise ValueError("cu_q and cu_k must describe the same number of sequences")
+    nv = None if n_valid is None else torch.as_tensor(n_valid, dtype=torch.int32, device=dev).contiguous()
+    idx = torch.empty((T, int(k)), dtype=torch.int32, device=dev)
+    sc = torch.empty((T, int(k)), dtype=torch.float32, device=dev) if with_scores else None
+    ws_n = lib().seqcomp_indexer_workspace_bytes(_i64p(hq), hq.size - 1)
+    if ws_n == ctypes.c_size_t(-1).value:
+        raise ValueError("malformed cu_q")
+    ws = _alloc_ws(ws_n, dev)
+    _check(lib().seqcomp_indexer_topk(_ptr(q), _ptr(w), _ptr(keys), q.shape[1], q.shape[2], _in_code(q),
+                                      _i64p(hq), _ptr(cq), _i64p(hk), _ptr(ck), hq.size - 1, _ptr(nv), int(k),
+                                      _ptr(idx), _ptr(sc), _ptr(ws), ws_n, _stream(dev)),
+           "seqcomp_indexer_topk")
+    return idx, sc

@@ -42,6 +42,9 @@ SIGNATURES = {
     "seqcomp_rope_store": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _i64p, _vp, _c_i64, _vp, _c_i64, ctypes.c_double,
                                     _vp, _c_i64, _vp, _vp, _vp, _vp, _size, _vp]),
     "seqcomp_rope_store_workspace_bytes": (_size, [_c_i64, _i64p, _c_i64]),
+    "seqcomp_indexer_topk": (_c_int, [_vp, _vp, _vp, _c_i64, _c_i64, _c_int, _i64p, _vp, _i64p, _vp, _c_i64,
+                                      _vp, _c_i64, _vp, _vp, _vp, _size, _vp]),
+    "seqcomp_indexer_workspace_bytes": (_size, [_i64p, _c_i64]),
 }
 
 _lib = None

@@ -444,4 +444,55 @@ int seqcomp_rope_store(const void* entries, int in_dtype, int64_t c, int64_t m, 
   return hip_status(e);
 }
 
+size_t seqcomp_indexer_workspace_bytes(const int64_t* cu_q_host, int64_t batch) {
+  int64_t T;
+  if (check_cu(cu_q_host, batch, &T) != SEQCOMP_OK) return (size_t)-1;
+  if (T == 0) return 0;
+  return round_up((size_t)count_tiles(cu_q_host, batch, 1, kIndexerTileQueries) * sizeof(TileRec), 256);
+}
+
+int seqcomp_indexer_topk(const void* q, const float* w, const void* keys, int64_t n_heads, int64_t head_dim,
+                         int in_dtype, const int64_t* cu_q_host, const int64_t* cu_q_dev,
+                         const int64_t* cu_k_host, const int64_t* cu_k_dev, int64_t batch,
+                         const int32_t* n_valid, int64_t k, int32_t* out_idx, float* out_score,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (in_dtype != SEQCOMP_BF16) return SEQCOMP_E_DTYPE;
+  if (n_heads != kIndexerHeads || head_dim != kIndexerDim) return SEQCOMP_E_UNSUPPORTED;
+  if (k < 1 || k > kIndexerMaxK) return SEQCOMP_E_UNSUPPORTED;
+  int64_t T = 0, N = 0;
+  int st = check_cu(cu_q_host, batch, &T);
+  if (st) return st;
+  if ((st = check_cu(cu_k_host, batch, &N))) return st;
+  // key offsets of a sequence (and of a ragged last stage) stay below 2^31 bytes
+  for (int64_t b = 0; b < batch; ++b)
+    if (cu_k_host[b + 1] - cu_k_host[b] >= (int64_t(1) << 23)) return SEQCOMP_E_UNSUPPORTED;
+  if (T == 0) return SEQCOMP_OK;
+  if (!q || !w || !cu_q_dev || !cu_k_dev || !out_idx || (N > 0 && !keys)) return SEQCOMP_E_NULL;
+  if (!aligned16(q) || !aligned16(w) || (keys && !aligned16(keys)) || !aligned16(cu_q_dev) ||
+      !aligned16(cu_k_dev) || !aligned16(out_idx) || (out_score && !aligned16(out_score)) ||
+      (n_valid && (reinterpret_cast<uintptr_t>(n_valid) & 3u)))
+    return SEQCOMP_E_ALIGN;
+  const size_t need = seqcomp_indexer_workspace_bytes(cu_q_host, batch);
+  Range ws_r;
+  if ((st = check_workspace(workspace, workspace_bytes, need, &ws_r))) return st;
+  Range reads[6];
+  int nr = 0;
+  reads[nr++] = range_of(q, (size_t)T * kIndexerHeads * kIndexerDim * 2);
+  reads[nr++] = range_of(w, (size_t)T * kIndexerHeads * 4);
+  if (keys) reads[nr++] = range_of(keys, (size_t)N * kIndexerDim * 2);
+  reads[nr++] = range_of(cu_q_dev, (size_t)(batch + 1) * 8);
+  reads[nr++] = range_of(cu_k_dev, (size_t)(batch + 1) * 8);
+  if (n_valid) reads[nr++] = range_of(n_valid, (size_t)T * 4);
+  const Range writes[3] = {range_of(out_idx, (size_t)T * k * 4),
+                           out_score ? range_of(out_score, (size_t)T * k * 4) : Range(), ws_r};
+  if ((st = check_alias(writes, 3, reads, nr))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TileRec* tiles = static_cast<TileRec*>(workspace);
+  const int n_tiles = (int)count_tiles(cu_q_host, batch, 1, kIndexerTileQueries);
+  hipError_t e = launch_plan(cu_q_dev, (int)batch, 1, kIndexerTileQueries, tiles, n_tiles, s);
+  if (e == hipSuccess)
+    e = launch_indexer_topk(q, w, keys, cu_k_dev, n_valid, tiles, n_tiles, (int)k, out_idx, out_score, s);
+  return hip_status(e);
+}
+
 }  // extern "C"

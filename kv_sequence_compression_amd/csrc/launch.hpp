@@ -67,6 +67,16 @@ hipError_t launch_rope_store(int in_dt, const void* entries, int c, int m, const
                              int64_t n_slots, const TileRec* tiles, int n_tiles, uint8_t* nope, float* scale,
                              uint16_t* rope, hipStream_t stream);
 
+// Lightning indexer: 64 heads of 128 bf16 dimensions; workgroups of 8
+// queries of one sequence (tiles from the planner with m = 1, tile_rows = 8).
+constexpr int kIndexerHeads = 64;
+constexpr int kIndexerDim = 128;
+constexpr int kIndexerTileQueries = 8;
+constexpr int kIndexerMaxK = 1024;
+hipError_t launch_indexer_topk(const void* q, const float* w, const void* keys, const int64_t* cu_k_dev,
+                               const int32_t* n_valid, const TileRec* tiles, int n_tiles, int k, int32_t* out_idx,
+                               float* out_score, hipStream_t stream);
+
 hipError_t launch_csa_fixup(int out_dt, const TileRec* tiles, int n_tiles, int c, const float* halo,
                             void* out, hipStream_t stream);
 

@@ -22,7 +22,14 @@ m = 4 for CSA, m' = 128 for HCA, ~1M tokens):
 
 Tensor ids: H=1, W_KVa=2, W_KVb=3, W_Za=4, W_Zb=5, B^a=6, B^b=7, W_KV=8,
 W_Z=9, B=10, lengths=11, outlier channels=12, C^a=13, C^b=14, Z^a=15,
-Z^b=16.
+Z^b=16, indexer queries q^I=17, head weights w^I=18, indexer keys=19.
+
+Lightning-indexer inputs (64 heads of 128 dims, the pages' n_h^I and c^I):
+queries and keys bf16 N(0, 1), head weights fp32 N(0, 1) (learned weights
+of either sign); or, for exact comparisons, small integers in [-3, 3] (every
+product and sum is then an integer well below 2^24, exact in fp32).  A query
+at position p of its sequence sees the compressed entries whose blocks of m
+tokens are complete, floor((p + 1) / m).
 """
 
 from __future__ import annotations
@@ -33,7 +40,7 @@ import numpy as np
 import torch
 
 TID = dict(H=1, W_KVa=2, W_KVb=3, W_Za=4, W_Zb=5, Ba=6, Bb=7, W_KV=8, W_Z=9, B=10,
-           lengths=11, outliers=12, Ca=13, Cb=14, Za=15, Zb=16)
+           lengths=11, outliers=12, Ca=13, Cb=14, Za=15, Zb=16, Qidx=17, Widx=18, Kidx=19)
 
 _TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -217,9 +224,57 @@ CONFIGS = {
                        d=7168, c=512, m_csa=4, m_hca=128, in_dtype="bf16",
                        out_dtype="fp8", bias_std=0.02, z_outlier_frac=0.01,
                        z_outlier_scale=30.0),
+    # Lightning indexer at 1M context: one sequence of 2^20 tokens -> 262144
+    # compressed indexer keys (m = 4); its last 4096 tokens query them
+    # (causal: floor((p + 1) / 4) visible), k = 1024.
+    "indexer_1m": dict(kind="indexer", n_tokens=1 << 20, m=4, n_queries=4096, k=1024),
 }
 
 
 def varlen_config_lengths(seed: int = 0) -> np.ndarray:
     cfg = CONFIGS["varlen_fp8"]
     return varlen_lengths(seed, cfg["batch"], cfg["len_lo"], cfg["len_hi"], cfg["len_mult"])
+
+
+# ------------------------------------------------------------ indexer inputs
+
+INDEXER_HEADS = 64     # n_h^I
+INDEXER_DIM = 128      # c^I
+
+
+def integers(shape, lo: int, hi: int, key, device="cpu", dtype="bf16") -> torch.Tensor:
+    """Seeded uniform integers in [lo, hi] stored as `dtype` (exact in bf16
+    for |v| <= 256)."""
+    rng = np.random.default_rng(list(key))
+    x = torch.from_numpy(rng.integers(lo, hi + 1, size=tuple(int(v) for v in shape)).astype(np.float32))
+    return x.to(_TORCH_DTYPES[dtype]).to(device)
+
+
+@dataclass
+class IndexerCase:
+    q: torch.Tensor            # [T x 64 x 128] bf16
+    w: torch.Tensor            # [T x 64] fp32
+    keys: torch.Tensor         # [N x 128] bf16
+    cu_q: np.ndarray
+    cu_k: np.ndarray
+
+
+def indexer_case(q_lengths, k_lengths, *, seed: int = 0, device="cpu", integer: bool = False) -> IndexerCase:
+    """Queries, head weights and compressed indexer keys of a packed batch:
+    sequence b has q_lengths[b] queries and k_lengths[b] keys."""
+    T, N = int(np.sum(q_lengths)), int(np.sum(k_lengths))
+    H, D = INDEXER_HEADS, INDEXER_DIM
+    if integer:
+        q = integers((T, H, D), -3, 3, (seed, TID["Qidx"]), device)
+        w = integers((T, H), -3, 3, (seed, TID["Widx"]), device, "f32")
+        keys = integers((N, D), -3, 3, (seed, TID["Kidx"]), device)
+    else:
+        q = normal((T, H, D), 1.0, (seed, TID["Qidx"]), device, "bf16")
+        w = normal((T, H), 1.0, (seed, TID["Widx"]), device, "f32")
+        keys = normal((N, D), 1.0, (seed, TID["Kidx"]), device, "bf16")
+    return IndexerCase(q, w, keys, cu_from_lengths(q_lengths), cu_from_lengths(k_lengths))
+
+
+def causal_visible(positions, m: int) -> np.ndarray:
+    """Entries visible to queries at `positions`: complete blocks of m tokens."""
+    return ((np.asarray(positions, dtype=np.int64) + 1) // m).astype(np.int32)

@@ -73,3 +73,47 @@ def entry_owner(cu: np.ndarray, m: int, idx: np.ndarray):
     starts = np.concatenate([[0], np.cumsum(counts)])
     seq = np.searchsorted(starts, idx, side="right") - 1
     return seq, idx - starts[seq]
+
+
+# ------------------------------------------------------------ indexer checks
+
+U32 = 2.0 ** -24   # fp32 unit roundoff
+
+
+def indexer_score_bound(Q, w, K, u=U32):
+    """Per-query a priori bound on |fp32 score - exact score| over all keys:
+    200 u max_s sum_h |w_h| sum_i |q_hi K_si|.  A dot product of 128 bf16
+    products (exact in fp32) takes at most 127 roundings, the weighted head
+    sum at most 66 (fused multiply-adds, two partial sums, one exchange add),
+    so the error is below (gamma_127 + gamma_66 + gamma_127 gamma_66) B
+    < 200 u B, with B = sum_h |w_h| sum_i |q_hi K_si|."""
+    Q, w, K = np.abs(Q), np.abs(w), np.abs(K)
+    T, H, c = Q.shape
+    B = np.einsum("th,ths->ts", w, (Q.reshape(T * H, c) @ K.T).reshape(T, H, -1))
+    return 200.0 * u * (B.max(axis=1) if B.shape[1] else np.zeros(T))
+
+
+def check_topk_valid(idx, sc, I, nv, k, beta):
+    """A selection is valid when scores differ from the oracle's by <= beta:
+    indices distinct, increasing and visible, min(k, visible) of them; returned
+    scores within beta of the oracle's; every key above the oracle's k-th
+    score + 2 beta selected and none below the k-th - 2 beta."""
+    idx = np.asarray(idx, dtype=np.int64)
+    for t in range(idx.shape[0]):
+        v = int(nv[t])
+        n = min(k, v)
+        sel = idx[t, :n]
+        assert np.all(idx[t, n:] == -1), t
+        assert np.all(np.diff(sel) > 0) and (n == 0 or (sel[0] >= 0 and sel[-1] < v)), t
+        if sc is not None:
+            assert np.all(np.isneginf(sc[t, n:])), t
+            err = np.abs(sc[t, :n] - I[t, sel])
+            assert np.all(err <= beta[t]), (t, err.max(), beta[t])
+        if v > k:
+            row = I[t, :v]
+            kth = np.sort(row)[::-1][k - 1]
+            must = np.nonzero(row > kth + 2 * beta[t])[0]
+            never = np.nonzero(row < kth - 2 * beta[t])[0]
+            s = set(sel.tolist())
+            assert all(int(x) in s for x in must), t
+            assert not any(int(x) in s for x in never), t

@@ -254,3 +254,55 @@ def test_rope_store_workspace(lib):
 ])
 def test_rope_store_rejects_bad_arguments(lib, kw, code):
     assert rope_store(lib, **kw) == S[code]
+
+
+CU_K_DEV = 0x50300000
+
+
+def indexer(lib, **kw):
+    a = dict(q=A, w=B_, keys=C_, H=64, D=128, in_dt=_lib.BF16, cu_q=_cu(0, 4096), cu_q_dev=CU_DEV,
+             cu_k=_cu(0, 262144), cu_k_dev=CU_K_DEV, nv=D_, k=1024, idx=OUT, sc=SCALE, ws=WS, ws_bytes=1 << 20)
+    a.update(kw)
+    cq, ck = a["cu_q"], a["cu_k"]
+    return lib.seqcomp_indexer_topk(a["q"], a["w"], a["keys"], a["H"], a["D"], a["in_dt"], _p(cq), a["cu_q_dev"],
+                                    _p(ck), a["cu_k_dev"], cq.size - 1, a["nv"], a["k"], a["idx"], a["sc"], a["ws"],
+                                    a["ws_bytes"], None)
+
+
+def test_indexer_workspace(lib):
+    f = lib.seqcomp_indexer_workspace_bytes
+    assert f(_p(_cu(0, 4096)), 1) == 512 * 16          # 512 tiles of 8 queries
+    assert f(_p(_cu(0, 9, 9, 10)), 3) == 256           # 3 tiles, rounded up to 256 bytes
+    assert f(_p(_cu(0, 0)), 1) == 0
+    assert f(_p(_cu(0, -1)), 1) == ctypes.c_size_t(-1).value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(in_dt=_lib.F32), "SEQCOMP_E_DTYPE"),
+    (dict(H=32), "SEQCOMP_E_UNSUPPORTED"),
+    (dict(D=64), "SEQCOMP_E_UNSUPPORTED"),
+    (dict(k=0), "SEQCOMP_E_UNSUPPORTED"),
+    (dict(k=1025), "SEQCOMP_E_UNSUPPORTED"),
+    (dict(cu_k=_cu(0, 1 << 23)), "SEQCOMP_E_UNSUPPORTED"),     # key offsets must stay below 2^31 bytes
+    (dict(cu_q=_cu(0, 5, 4), cu_k=_cu(0, 5, 9)), "SEQCOMP_E_SEQLENS"),
+    (dict(cu_k=_cu(1, 9)), "SEQCOMP_E_SEQLENS"),
+    (dict(q=0), "SEQCOMP_E_NULL"),
+    (dict(keys=0), "SEQCOMP_E_NULL"),
+    (dict(idx=0), "SEQCOMP_E_NULL"),
+    (dict(cu_k_dev=0), "SEQCOMP_E_NULL"),
+    (dict(w=B_ + 4), "SEQCOMP_E_ALIGN"),
+    (dict(nv=D_ + 2), "SEQCOMP_E_ALIGN"),
+    (dict(ws_bytes=16), "SEQCOMP_E_WORKSPACE"),
+    (dict(idx=A + 4096), "SEQCOMP_E_ALIAS"),                     # selection over the queries
+    (dict(sc=OUT + 4096), "SEQCOMP_E_ALIAS"),                    # scores over the selection
+    (dict(ws=C_ + 256), "SEQCOMP_E_ALIAS"),                      # workspace over the keys
+    (dict(nv=0, sc=0, idx=0), "SEQCOMP_E_NULL"),                 # n_valid and scores are optional, idx is not
+])
+def test_indexer_rejects_bad_arguments(lib, kw, code):
+    assert indexer(lib, **kw) == S[code]
+
+
+def test_indexer_empty_calls_launch_nothing(lib):
+    # no queries: OK before any pointer is looked at; keys may be absent when there are none
+    assert indexer(lib, cu_q=_cu(0, 0), q=0, w=0, idx=0, sc=0, ws=0, ws_bytes=0) == S["SEQCOMP_OK"]
+    assert indexer(lib, cu_k=_cu(0, 0), keys=0, cu_q=_cu(0, 0), q=0, w=0, idx=0, ws=0) == S["SEQCOMP_OK"]
