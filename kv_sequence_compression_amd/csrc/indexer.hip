@@ -7,29 +7,32 @@
 // scores never reach memory: ReLU needs no normalisation over s, so each one
 // is judged against a running threshold the moment it is computed.
 //
-// One workgroup takes 8 queries of one sequence (2 per wavefront) and sweeps
-// their keys in stages of 64.  The dot products are a dense contraction: for
-// a block of 32 keys a wave runs, per query, two 32-head row blocks of
-// v_mfma_f32_32x32x16_bf16 over K = 128 (8 MFMAs each), with the queries'
-// A fragments held in registers for the whole sweep and the key fragments
-// read from LDS.  The 32x32 accumulator leaves lane l with key l % 32 and 16
-// of the 64 heads (rows 8 g + 4 (l / 32) + 0..3), so the ReLU and the
-// head-weighted sum are 32 fused multiply-adds per lane and query, and one
-// exchange between lanes l and l ^ 32 (v_permlane32_swap) completes both
-// queries' scores at once: lanes 0..31 hold query 0's, lanes 32..63 query 1's.
+// One workgroup takes 8 queries of one sequence, one per wavefront (two
+// wavefronts per SIMD, so one's MFMAs run while the other forms scores), and
+// sweeps their keys in stages of 64.  The dot products are a dense
+// contraction: for a block of 32 keys a wave runs two 32-head row blocks of
+// v_mfma_f32_32x32x16_bf16 over K = 128 (8 MFMAs each), with its query's A
+// fragments held in registers for the whole sweep and the key fragments read
+// from LDS.  The 32x32 accumulator leaves lane l with key l % 32 and 16 of
+// the 64 heads (rows 8 g + 4 (l / 32) + 0..3 of each row block), so the ReLU
+// and the head-weighted sum are 32 fused multiply-adds per lane, and one
+// exchange between lanes l and l ^ 32 (v_permlane32_swap) completes the
+// score.  Within a wave the MFMAs of one block are issued before the scores
+// of the previous block are formed (a software pipeline over two
+// accumulator sets).
 //
 // Selection: each query owns a candidate buffer of 1536 (score, key) slots in
 // LDS and a threshold tau, the k-th best score seen so far (-inf until k
 // keys were kept).  A visible key whose score beats tau is appended (ballot
 // + lane prefix counts; keys arrive in increasing order, so the buffer stays
-// sorted by key).  When a buffer could overflow on the next block, the wave
-// finds the k-th best candidate by a radix select on order-preserving 32-bit
-// keys of the scores (4 passes of 8-bit histograms in LDS), keeps the k best
-// in place -- a stable compaction, so ties at the threshold go to the smaller
-// key index -- and raises tau to that score.  A later key with a score equal
-// to tau has a larger index and so ranks below every kept one: the strict
-// test "score > tau" is exact.  At the end of the sweep one more compaction
-// leaves the k best, listed by increasing key index.
+// sorted by key).  When a buffer could overflow within the next stage, the
+// wave finds the k-th best candidate by a radix select on order-preserving
+// 32-bit keys of the scores (4 passes of 8-bit histograms in LDS), keeps the
+// k best in place -- a stable compaction, so ties at the threshold go to the
+// smaller key index -- and raises tau to that score.  A later key with a
+// score equal to tau has a larger index and so ranks below every kept one:
+// the strict test "score > tau" is exact.  At the end of the sweep one more
+// compaction leaves the k best, listed by increasing key index.
 //
 // Keys travel global -> LDS directly (buffer_load ... lds, 16 bytes a lane,
 // whole 128-byte lines), through a ring of 3 stages (48 KiB), two stages
@@ -44,7 +47,7 @@ namespace seqcomp {
 
 namespace {
 
-constexpr int kIxThreads = 256;
+constexpr int kIxThreads = 512;                              // 8 waves: one query each, 2 per SIMD
 constexpr int kIxKeyBytes = kIndexerDim * 2;                  // one bf16 key: 256 bytes
 constexpr int kIxStageKeys = 64;
 constexpr int kIxStages = 3;
@@ -53,7 +56,8 @@ constexpr int kIxCap = 1536;                                  // candidate slots
 constexpr int kIxCandOff = kIxStages * kIxStageBytes;         // 48 KiB of key stages
 constexpr int kIxIdxOff = kIxCandOff + kIndexerTileQueries * kIxCap * 4;
 constexpr int kIxHistOff = kIxIdxOff + kIndexerTileQueries * kIxCap * 4;   // + 96 KiB of candidates
-constexpr int kIxLdsBytes = kIxHistOff + 4 * 256 * 4;         // + 4 KiB of histograms = 148 KiB
+constexpr int kIxFlagOff = kIxHistOff + 8 * 256 * 4;         // + 8 KiB of histograms
+constexpr int kIxLdsBytes = kIxFlagOff + 16;                  // + compaction flags: ~152 KiB
 static_assert(kIxCap >= kIndexerMaxK + 64, "after a compaction a key block must still fit");
 static_assert(kIndexerHeads == 64 && kIndexerDim == 128, "fragment layout assumes 64 heads of 128 dims");
 
@@ -177,7 +181,6 @@ __device__ __forceinline__ float compact_candidates(float* cs, int32_t* ci, int 
 __global__ __launch_bounds__(kIxThreads, 1) void indexer_topk_kernel(IxArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[kIxLdsBytes];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const bool upper = lane >= 32;
   const TileRec tile = a.tiles[a.n_tiles - 1 - (int)blockIdx.x];   // later (longer) tiles first
   const int seq = tile_seq(tile.flags);
   const int64_t q0 = tile.row_start;
@@ -186,164 +189,178 @@ __global__ __launch_bounds__(kIxThreads, 1) void indexer_topk_kernel(IxArgs a) {
   const int nk = (int)(a.cu_k[seq + 1] - kbase);
 
   // Visible keys of the tile's queries; the sweep covers the longest.
-  int nv_max = 0, nv0 = 0, nv1 = 0;
+  int nv_max = 0, my_nv = 0;
 #pragma unroll
   for (int j = 0; j < kIndexerTileQueries; ++j) {
     int v = 0;
     if (j < nq) v = a.n_valid ? min(max(a.n_valid[q0 + j], 0), nk) : nk;
     nv_max = max(nv_max, v);
-    if (j == 2 * w) nv0 = v;
-    if (j == 2 * w + 1) nv1 = v;
+    if (j == w) my_nv = v;
   }
-  const int my_nv = upper ? nv1 : nv0;
 
-  // The wave's two queries (a missing one reads the tile's first query and
-  // keeps nothing): A fragments of the 4 row blocks (query j, heads
-  // 32 b + l % 32) for the 8 k-steps, and the weights of the lane's 16 heads
-  // per row block.
-  bf16x8_t qa[4][8];
-  float wv[4][16];
+  // The wave's query (a missing one reads the tile's first query and keeps
+  // nothing): A fragments of its 2 row blocks (heads 32 b + l % 32) for the
+  // 8 k-steps, and the weights of the lane's 16 heads per row block.
+  bf16x8_t qa[2][8];
+  float wv[2][16];
+  {
+    const int64_t t = q0 + (w < nq ? w : 0);
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    const int j = 2 * w + (rb >> 1);
-    const int64_t t = q0 + (j < nq ? j : 0);
-    const char* row = a.q + ((t * kIndexerHeads + 32 * (rb & 1) + (lane & 31)) * kIxKeyBytes) + (lane >> 5) * 16;
+    for (int rb = 0; rb < 2; ++rb) {
+      const char* row = a.q + ((t * kIndexerHeads + 32 * rb + (lane & 31)) * kIxKeyBytes) + (lane >> 5) * 16;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qa[rb][kk] = __builtin_bit_cast(bf16x8_t, ld16(row + kk * 32));
+      for (int kk = 0; kk < 8; ++kk) qa[rb][kk] = __builtin_bit_cast(bf16x8_t, ld16(row + kk * 32));
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const float4 v = *reinterpret_cast<const float4*>(a.w + t * kIndexerHeads + 32 * (rb & 1) + 8 * g +
-                                                        4 * (lane >> 5));
-      wv[rb][4 * g + 0] = v.x;
-      wv[rb][4 * g + 1] = v.y;
-      wv[rb][4 * g + 2] = v.z;
-      wv[rb][4 * g + 3] = v.w;
+      for (int g = 0; g < 4; ++g) {
+        const float4 v =
+            *reinterpret_cast<const float4*>(a.w + t * kIndexerHeads + 32 * rb + 8 * g + 4 * (lane >> 5));
+        wv[rb][4 * g + 0] = v.x;
+        wv[rb][4 * g + 1] = v.y;
+        wv[rb][4 * g + 2] = v.z;
+        wv[rb][4 * g + 3] = v.w;
+      }
     }
   }
 
-  float* const cand_s = reinterpret_cast<float*>(lds + kIxCandOff) + (2 * w) * kIxCap;
-  int32_t* const cand_i = reinterpret_cast<int32_t*>(lds + kIxIdxOff) + (2 * w) * kIxCap;
+  float* const cand_s = reinterpret_cast<float*>(lds + kIxCandOff) + w * kIxCap;
+  int32_t* const cand_i = reinterpret_cast<int32_t*>(lds + kIxIdxOff) + w * kIxCap;
   uint32_t* const hist = reinterpret_cast<uint32_t*>(lds + kIxHistOff) + w * 256;
-  float* const my_s = cand_s + (upper ? kIxCap : 0);
-  int32_t* const my_i = cand_i + (upper ? kIxCap : 0);
 
-  // Copies of one stage: wave w fills rows 16 w .. 16 w + 15 with 4 copies of
+  // Copies of one stage: wave w fills rows 8 w .. 8 w + 7 with 2 copies of
   // 1 KiB (4 rows each); lane p writes slot p & 15 of row p >> 4 of its 4,
   // which holds chunk (p & 15) ^ (row & 15) of that key.
   const __amdgpu_buffer_rsrc_t ksrc = ranged_rsrc(a.keys + kbase * kIxKeyBytes, (uint32_t)nk * kIxKeyBytes);
-  uint32_t voff[4];
+  uint32_t voff[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (w * 4 + i) * 4 + (lane >> 4);
+  for (int i = 0; i < 2; ++i) {
+    const int r = (w * 2 + i) * 4 + (lane >> 4);
     voff[i] = (uint32_t)(r * kIxKeyBytes + (((lane & 15) ^ (r & 15)) * 16));
   }
   const auto issue_stage = [&](int s) {
-    char* dst = lds + (s % kIxStages) * kIxStageBytes + w * 4 * 1024;
+    char* dst = lds + (s % kIxStages) * kIxStageBytes + w * 2 * 1024;
     const uint32_t so = (uint32_t)s * kIxStageBytes;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ksrc, (lds_void_t*)(dst + i * 1024), 16, voff[i] + so, 0, 0, 0);
   };
 
   const int n_st = (nv_max + kIxStageKeys - 1) / kIxStageKeys;
+  uint8_t* const flags = reinterpret_cast<uint8_t*>(lds + kIxFlagOff);
+  flags[w] = 0;
+  flags[8 + w] = 0;
   if (n_st > 0) issue_stage(0);
   if (n_st > 1) issue_stage(1);
 
-  float tau0 = -INFINITY, tau1 = -INFINITY;
-  int cnt0 = 0, cnt1 = 0;
   float tau = -INFINITY;
+  int cnt = 0;
   const int r = lane & 31;          // key row of the lane's B fragment and score
   const int k = a.k;
 
+  const auto compact = [&]() {
+    tau = compact_candidates(cand_s, cand_i, cnt, k, hist, lane);
+    cnt = k;
+  };
+  // B fragments of one block of 32 keys (rows 32 bi .. 32 bi + 31 of a stage).
+  const auto read_block = [&](const char* st, int bi, f32x4_t (&bf)[8]) {
+    const char* kr = st + (bi * 32 + r) * kIxKeyBytes;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      bf[kk] = *reinterpret_cast<const f32x4_t*>(kr + (((2 * kk + (lane >> 5)) ^ (r & 15)) * 16));
+  };
+  // Dot products of the query's 2 row blocks with one block of keys.
+  const auto mma_block = [&](const f32x4_t (&bf)[8], f32x16_t (&acc)[2]) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+      acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[rb][0], __builtin_bit_cast(bf16x8_t, bf[0]),
+                                                        f32x16_t{}, 0, 0, 0);
+#pragma unroll
+    for (int kk = 1; kk < 8; ++kk)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+        acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[rb][kk], __builtin_bit_cast(bf16x8_t, bf[kk]),
+                                                          acc[rb], 0, 0, 0);
+  };
+  // ReLU and head-weighted sum of a finished block: every lane ends with the
+  // score of key l % 32 of the block.  ReLU is an integer max on the bit
+  // pattern (negative floats are negative integers), one instruction.
+  const auto block_score = [&](const f32x16_t (&acc)[2]) {
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      s0 = fmaf(wv[0][e], __int_as_float(max(__float_as_int(acc[0][e]), 0)), s0);
+      s1 = fmaf(wv[1][e], __int_as_float(max(__float_as_int(acc[1][e]), 0)), s1);
+    }
+    const float p = s0 + s1;
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+    // lanes < 32: own half (rows 8 g + 0..3) + the other (rows 8 g + 4..7)
+    return lane < 32 ? p + __uint_as_float(sw[1]) : __uint_as_float(sw[0]) + p;
+  };
+  // Appends the block's keys (lanes < 32) whose score beats the threshold.
+  const auto append = [&](float score, int key0) {
+    const int key = key0 + r;
+    const bool pass = lane < 32 && key < my_nv && score > tau;
+    const uint64_t m = __ballot(pass);
+    if (m) {
+      if (pass) {
+        const int pos = cnt + (int)__builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u);
+        cand_s[pos] = score;
+        cand_i[pos] = key;
+      }
+      cnt += __popcll(m);
+      wave_lds_sync();
+    }
+  };
+
+  // Software pipeline over blocks: the MFMAs of a block run while the
+  // previous block's scores are formed and judged.  Iteration s multiplies
+  // blocks (s, 0) and (s, 1) and finishes (s - 1, 1) and (s, 0); a query
+  // gains at most 64 candidates per iteration.  Compactions are taken at
+  // iteration starts, by every wave at once when any query of the tile is
+  // close to full, so that one wave's compaction does not hold up the others
+  // at the next barrier one query at a time.
+  f32x16_t acc0[2], acc1[2];
+  acc1[0] = f32x16_t{};
+  acc1[1] = f32x16_t{};
+  int prev_key0 = 0x7fffff00;       // no previous block: no key passes
+  f32x4_t bf0[8], bf1[8];
 #pragma unroll 1
   for (int s = 0; s < n_st; ++s) {
-    if (s + 1 < n_st) wait_vmcnt<4>();
-    else wait_vmcnt<0>();
+    // own copies of stage s landed, own LDS writes (flags) done
+    if (s + 1 < n_st) wait_vmcnt_lgkm0<2>();
+    else wait_vmcnt_lgkm0<0>();
     lds_barrier();                  // stage s is in; every wave is done with stage s - 1
     if (s + 2 < n_st) issue_stage(s + 2);
+    const uint32_t* fl = reinterpret_cast<const uint32_t*>(flags + 8 * (s & 1));
+    if ((fl[0] | fl[1]) && cnt > k) compact();
     const char* st = lds + (s % kIxStages) * kIxStageBytes;
-#pragma unroll
-    for (int bi = 0; bi < 2; ++bi) {
-      const char* kr = st + (bi * 32 + r) * kIxKeyBytes;
-      f32x4_t bf[8];
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk)
-        bf[kk] = *reinterpret_cast<const f32x4_t*>(kr + (((2 * kk + (lane >> 5)) ^ (r & 15)) * 16));
-      f32x16_t acc[4];
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[rb][e] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-          acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[rb][kk], __builtin_bit_cast(bf16x8_t, bf[kk]),
-                                                            acc[rb], 0, 0, 0);
-      float p[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          s0 = fmaf(wv[2 * j][e], fmaxf(acc[2 * j][e], 0.f), s0);
-          s1 = fmaf(wv[2 * j + 1][e], fmaxf(acc[2 * j + 1][e], 0.f), s1);
-        }
-        p[j] = s0 + s1;
-      }
-      // lanes < 32: query 0's halves; lanes >= 32: query 1's
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[1]), false, false);
-      const float score = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-      const int key = s * kIxStageKeys + bi * 32 + r;
-      const bool pass = key < my_nv && score > tau;
-      const uint64_t m = __ballot(pass);
-      if (m) {
-        const uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
-        const int pos = upper ? cnt1 + (int)__builtin_amdgcn_mbcnt_hi(hi, 0u)
-                              : cnt0 + (int)__builtin_amdgcn_mbcnt_lo(lo, 0u);
-        if (pass) {
-          my_s[pos] = score;
-          my_i[pos] = key;
-        }
-        cnt0 += __popc(lo);
-        cnt1 += __popc(hi);
-        wave_lds_sync();
-#pragma unroll 1
-        while (cnt0 > kIxCap - 32 || cnt1 > kIxCap - 32) {
-          const int j = cnt0 > kIxCap - 32 ? 0 : 1;
-          const float t = compact_candidates(cand_s + j * kIxCap, cand_i + j * kIxCap, j ? cnt1 : cnt0, k, hist,
-                                             lane);
-          if (j) {
-            cnt1 = k;
-            tau1 = t;
-          } else {
-            cnt0 = k;
-            tau0 = t;
-          }
-        }
-        tau = upper ? tau1 : tau0;
-      }
-    }
+    read_block(st, 0, bf0);
+    mma_block(bf0, acc0);
+    const float sc_prev = block_score(acc1);
+    read_block(st, 1, bf1);
+    append(sc_prev, prev_key0);
+    mma_block(bf1, acc1);
+    const float sc0 = block_score(acc0);
+    append(sc0, s * kIxStageKeys);
+    prev_key0 = s * kIxStageKeys + 32;
+    flags[8 * ((s + 1) & 1) + w] = cnt > kIxCap - 64 ? 1 : 0;
+  }
+  if (n_st > 0) {
+    if (cnt > kIxCap - 32) compact();
+    append(block_score(acc1), prev_key0);
   }
 
   // Final selection and output (keys in increasing order, -1 / -inf after
   // the last selected one).
-#pragma unroll 1
-  for (int j = 0; j < 2; ++j) {
-    const int qj = 2 * w + j;
-    if (qj >= nq) break;
-    int n = j ? cnt1 : cnt0;
-    float* cs = cand_s + j * kIxCap;
-    int32_t* ci = cand_i + j * kIxCap;
-    if (n > k) {
-      compact_candidates(cs, ci, n, k, hist, lane);
-      n = k;
+  if (w < nq) {
+    if (cnt > k) {
+      compact_candidates(cand_s, cand_i, cnt, k, hist, lane);
+      cnt = k;
     }
-    const int64_t t = q0 + qj;
+    const int64_t t = q0 + w;
     for (int i = lane; i < k; i += 64) {
-      const bool have = i < n;
-      a.out_idx[t * k + i] = have ? ci[i] : -1;
-      if (a.out_score) a.out_score[t * k + i] = have ? cs[i] : -INFINITY;
+      const bool have = i < cnt;
+      a.out_idx[t * k + i] = have ? cand_i[i] : -1;
+      if (a.out_score) a.out_score[t * k + i] = have ? cand_s[i] : -INFINITY;
     }
   }
 }
