@@ -58,16 +58,26 @@ def _traffic(kernel_key: str):
         return None
 
 
+def _progress(msg: str):
+    """One line per finished phase on stderr (the JSON line alone goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def _blas_threads() -> int:
+    """Threads of the BLAS pool numpy uses (the oracle's only parallel part)."""
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([p.get("num_threads", 1) for p in threadpool_info()] or [1]))
+    except Exception:  # noqa: BLE001
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(case_csa, case_hca, sample_tokens: int):
     """The float64 oracle, as it stands, on the first `sample_tokens` tokens
     (whole sequences first, the last one truncated to a multiple of 128)."""
     import torch
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = os.cpu_count() or 1
+    threads = _blas_threads()
     cu = case_csa.cu_seqlens
     H = case_csa.H[:sample_tokens].to("cpu", torch.float64).numpy()
     W = {k: v.to("cpu", torch.float64).numpy() for k, v in case_csa.W.items()}
@@ -176,6 +186,54 @@ def rope_store(sc, torch, csa, steps):
             "us": ms * 1e3, "entries_per_s": E / (ms * 1e-3), "gbs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS}
 
 
+def lightning_indexer(sc, synth, torch, steps, cpu_queries=2):
+    """Lightning indexer at 1M context: 262144 compressed indexer keys
+    (2^20 tokens, m = 4), the sequence's last 4096 tokens as queries (causal
+    visibility), 64 heads x 128 dims bf16, fp32 head weights; k = 1024 and
+    512.  MFMA-bound: 2 * 64 * 128 flops per visible (query, key) pair."""
+    cfg = synth.CONFIGS["indexer_1m"]
+    n_tok, T, m = cfg["n_tokens"], cfg["n_queries"], cfg["m"]
+    dev = torch.device("cuda:0")
+    case = synth.indexer_case([T], [n_tok // m], seed=0, device=dev)
+    nv = synth.causal_visible(np.arange(n_tok - T, n_tok), m)
+    pairs = float(nv.astype(np.float64).sum())
+    flops = 2.0 * synth.INDEXER_HEADS * synth.INDEXER_DIM * pairs
+    res = {"workload": f"indexer_1m: {n_tok // m} keys (n={n_tok}, m={m}), the last {T} tokens query with causal "
+                       f"visibility, 64 heads x 128 bf16, fp32 head weights; ReLU scores + top-k",
+           "flops_per_call": flops}
+    for k in (cfg["k"], 512):
+        call = lambda: sc.indexer_topk(case.q, case.w, case.keys, k, case.cu_q, case.cu_k, nv)
+        call()
+        torch.cuda.synchronize()
+        ev = _events(torch, 2)
+        ev[0].record()
+        for _ in range(steps):
+            call()
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / steps
+        tf = flops / (ms * 1e-3) / 1e12
+        res[f"k={k}"] = {"ms": ms, "queries_per_s": T / (ms * 1e-3), "tflops": tf,
+                         "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                      "frac": tf / PEAK_BF16_TFLOPS, "traffic": _traffic("indexer_1m_topk"),
+                                      "kernel": "indexer call (planner + indexer_topk_kernel)"}}
+    # the float64 oracle on a few of the same queries, this host's cores
+    import oracle
+    rows = np.arange(T - cpu_queries, T)
+    Q = case.q[-cpu_queries:].double().cpu().numpy()
+    w = case.w[-cpu_queries:].double().cpu().numpy()
+    K = case.keys.double().cpu().numpy()
+    t0 = time.perf_counter()
+    I = oracle.index_scores(Q, w, K, n_valid=nv[rows])
+    oracle.top_k(I, cfg["k"])
+    dt = time.perf_counter() - t0
+    res["cpu_oracle"] = {"queries_per_s": cpu_queries / dt, "sample": f"{cpu_queries} queries x {n_tok // m} keys, "
+                         f"k={cfg['k']}", "cores": _blas_threads(), "kind": "oracle"}
+    del case
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -186,7 +244,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-pool", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the indexer-key compressor and decode-append measurements")
+                    help="skip the indexer-key compressor, decode-append, RoPE-store and lightning-indexer "
+                         "measurements")
     ap.add_argument("--profile-copy", action="store_true",
                     help="first run a plain 1 GiB device copy (torch copy kernel): the known-size reference that "
                          "scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -266,6 +325,7 @@ def main():
                      "kernel": "fused CSA call (tile kernel + planner + halo fix-up + fp8 encoder)",
                      "algorithmic_flops_per_launch": flops_csa},
     }
+    _progress("compressor step timed")
     if not args.no_pool:
         pc = synth.pool_case(1 << 20, 512, seed=0, dtype="bf16", device=dev, bias_std=0.02)
         st, pb = pc.streams, pc.biases
@@ -301,10 +361,17 @@ def main():
         del pc, st
         torch.cuda.empty_cache()
 
+    if not args.no_pool:
+        _progress("pooling-only path measured")
     if not args.no_extras:
         out["indexer_keys"] = indexer_keys(sc, synth, torch, csa, lengths, args.steps)
+        _progress("indexer-key compressor measured")
         out["decode_append"] = decode_append(sc, torch, csa, (64, 1024, 4096), args.steps)
+        _progress("decode append measured")
         out["rope_store"] = rope_store(sc, torch, csa, args.steps)
+        _progress("RoPE store measured")
+        out["lightning_indexer"] = lightning_indexer(sc, synth, torch, args.steps)
+        _progress("lightning indexer measured")
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(csa, hca, args.cpu_sample_tokens)

@@ -95,87 +95,133 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// Keeps the k best of the n > k candidates (cs: scores, ci: keys, stored by
-// increasing key) in place and in key order; returns the k-th best score.
-// Called by the whole wave; hist is the wave's 256 counters.
-__device__ __forceinline__ float compact_candidates(float* cs, int32_t* ci, int n, int k, uint32_t* hist, int lane) {
-  // Radix select of the k-th largest order key, 8 bits at a time from the top:
-  // `prefix` holds the bits fixed so far, `need` the rank still sought among
-  // the candidates that share them.
-  uint32_t prefix = 0;
-  int need = k;
+constexpr int kIxSlotsPerLane = kIxCap / 64;                 // candidate slots a lane holds in a compaction
+static_assert(kIxCap % 64 == 0, "candidate buffer in whole wave rows");
+
+// Order key of the k-th best candidate, by radix selection on the wave's
+// register copy u[] of the candidates' order keys (slot lane + 64 j; empty
+// slots hold 0, below every real key).  Only the bits below the candidates'
+// common prefix are searched, 8 at a time from the top: each pass counts the
+// candidates that match the bits fixed so far per value of the next digit
+// (histogram in LDS), and a suffix scan over the bins finds the digit of the
+// k-th best.  Returns the bits fixed so far with the rest zero: after the
+// last pass (`exact` set) the k-th best key itself, and `need` says how many
+// candidates equal to it belong to the k best; else the lower edge of the
+// k-th best's bin, with at most `limit` candidates at or above it.  EXACT
+// runs every pass; otherwise passes stop once that edge keeps few enough.
+template <bool EXACT>
+__device__ __forceinline__ uint32_t select_kth(const uint32_t (&u)[kIxSlotsPerLane], int k, int limit,
+                                               uint32_t* hist, int lane, int& need, bool& exact) {
+  uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+  for (int j = 0; j < kIxSlotsPerLane; ++j) {
+    if (u[j] != 0u) lo = min(lo, u[j]);
+    hi = max(hi, u[j]);
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, off, 64));
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, off, 64));
+  }
+  int remaining = lo == hi ? 0 : 32 - __builtin_clz(lo ^ hi);   // low bits that differ
+  uint32_t prefix = remaining == 32 ? 0u : (hi >> remaining) << remaining;
+  need = k;
 #pragma unroll 1
-  for (int shift = 24; shift >= 0; shift -= 8) {
-#pragma unroll
-    for (int b = 0; b < 4; ++b) hist[lane * 4 + b] = 0u;
+  while (remaining > 0) {
+    const int width = min(8, remaining), shift = remaining - width;
+    const uint32_t dmask = (1u << width) - 1u;
+    *reinterpret_cast<uint4*>(hist + lane * 4) = make_uint4(0u, 0u, 0u, 0u);
     wave_lds_sync();
-    const uint32_t fixed = shift == 24 ? 0u : (0xffffffffu << (shift + 8));
-#pragma unroll 4
-    for (int i = lane; i < n; i += 64) {
-      const uint32_t u = order_key(cs[i]);
-      if ((u & fixed) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+#pragma unroll
+    for (int j = 0; j < kIxSlotsPerLane; ++j) {
+      const bool match = u[j] != 0u && (remaining == 32 || (u[j] >> remaining) == (prefix >> remaining));
+      if (match) atomicAdd(&hist[(u[j] >> shift) & dmask], 1u);
     }
     wave_lds_sync();
-    uint32_t h[4], tot = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      h[b] = hist[lane * 4 + b];
-      tot += h[b];
-    }
-    // candidates in the bins of higher lanes (inclusive suffix sum minus own)
-    uint32_t suf = tot;
+    const uint4 h4 = *reinterpret_cast<const uint4*>(hist + lane * 4);
+    const uint32_t h[4] = {h4.x, h4.y, h4.z, h4.w};
+    const uint32_t tot = h[0] + h[1] + h[2] + h[3];
+    uint32_t suf = tot;                                          // inclusive suffix sum over lanes
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const uint32_t y = __shfl_down(suf, off, 64);
       if (lane + off < 64) suf += y;
     }
-    uint32_t above = suf - tot;
-    int bin = -1, rest = 0;
+    uint32_t above = suf - tot;                                  // candidates in higher lanes' bins
+    int bin = -1, rest = 0, in_bin = 0;
 #pragma unroll
     for (int b = 3; b >= 0; --b) {
       if (bin < 0 && above < (uint32_t)need && above + h[b] >= (uint32_t)need) {
         bin = lane * 4 + b;
         rest = need - (int)above;
+        in_bin = (int)h[b];
       }
       above += h[b];
     }
-    const uint64_t found = __ballot(bin >= 0);
-    const int src = __builtin_ctzll(found);
+    const int src = __builtin_ctzll(__ballot(bin >= 0));
     bin = __shfl(bin, src, 64);
     rest = __shfl(rest, src, 64);
+    in_bin = __shfl(in_bin, src, 64);
     prefix |= (uint32_t)bin << shift;
+    remaining = shift;
+    // candidates kept by the bin's lower edge: the k - need above the
+    // matching set, need - rest above the bin within it, and the bin
+    const int at_edge = k - rest + in_bin;
     need = rest;
+    if (!EXACT && at_edge <= limit) break;
   }
-  // Stable in-place compaction: every candidate above the k-th, and the first
-  // `need` (smallest keys) of those equal to it.  Writes land below the
-  // chunk being read, and all of a chunk's reads complete before its writes.
-  int kept = 0, ties = 0;
-#pragma unroll 1
-  for (int base = 0; base < n; base += 64) {
-    const int i = base + lane;
-    float s = 0.f;
-    int32_t key = 0;
-    uint32_t u = 0;
-    if (i < n) {
-      s = cs[i];
-      key = ci[i];
-      u = order_key(s);
+  exact = remaining == 0;
+  return prefix;
+}
+
+// Compacts the n > k candidates (cs: scores, ci: keys, stored by increasing
+// key) in place and in key order.  EXACT: keeps exactly the k best (ties to
+// the smaller key) and returns the k-th best score.  Otherwise keeps at least
+// the k best and at most 128 slots short of a full buffer -- every candidate
+// at or above the lower edge of the k-th best's radix bin, or the exact k
+// best when the passes run out -- and returns a threshold no higher than the
+// k-th best (a later key must beat it to be a candidate; one equal to the
+// k-th best ranks below it, having the larger index).  The number kept goes
+// to `kept`.
+template <bool EXACT>
+__device__ __forceinline__ float compact_candidates(float* cs, int32_t* ci, int n, int k, uint32_t* hist, int lane,
+                                                    int& kept) {
+  uint32_t u[kIxSlotsPerLane];
+  int32_t id[kIxSlotsPerLane];
+#pragma unroll
+  for (int j = 0; j < kIxSlotsPerLane; ++j) {
+    const int i = lane + 64 * j;
+    u[j] = i < n ? order_key(cs[i]) : 0u;
+    id[j] = i < n ? ci[i] : 0;
+  }
+  int need;
+  bool exact;
+  const uint32_t cut = select_kth<EXACT>(u, k, kIxCap - 128, hist, lane, need, exact);
+  // Stable compaction: reads are all in registers, so writes may land anywhere below.
+  int out = 0, ties = 0;
+#pragma unroll
+  for (int j = 0; j < kIxSlotsPerLane; ++j) {
+    bool keep;
+    if (exact) {
+      const bool eq = u[j] == cut;
+      const uint64_t eqm = __ballot(eq);
+      keep = u[j] > cut || (eq && ties + lanes_below(eqm) < need);
+      ties += __popcll(eqm);
+    } else {
+      keep = u[j] >= cut && u[j] != 0u;
     }
-    const bool eq = i < n && u == prefix;
-    const uint64_t eqm = __ballot(eq);
-    const bool keep = (i < n && u > prefix) || (eq && ties + lanes_below(eqm) < need);
     const uint64_t km = __ballot(keep);
-    wave_lds_sync();
     if (keep) {
-      const int p = kept + lanes_below(km);
-      cs[p] = s;
-      ci[p] = key;
+      const int p = out + lanes_below(km);
+      cs[p] = order_key_value(u[j]);
+      ci[p] = id[j];
     }
-    kept += __popcll(km);
-    ties += __popcll(eqm);
+    out += __popcll(km);
   }
   wave_lds_sync();
-  return order_key_value(prefix);
+  kept = out;
+  if (exact) return order_key_value(cut);
+  return cut <= 0x007fffffu ? -INFINITY : order_key_value(cut);   // 0x007fffff: the key of -inf
 }
 
 __global__ __launch_bounds__(kIxThreads, 1) void indexer_topk_kernel(IxArgs a) {
@@ -256,10 +302,7 @@ __global__ __launch_bounds__(kIxThreads, 1) void indexer_topk_kernel(IxArgs a) {
   const int r = lane & 31;          // key row of the lane's B fragment and score
   const int k = a.k;
 
-  const auto compact = [&]() {
-    tau = compact_candidates(cand_s, cand_i, cnt, k, hist, lane);
-    cnt = k;
-  };
+  const auto compact = [&]() { tau = compact_candidates<false>(cand_s, cand_i, cnt, k, hist, lane, cnt); };
   // B fragments of one block of 32 keys (rows 32 bi .. 32 bi + 31 of a stage).
   const auto read_block = [&](const char* st, int bi, f32x4_t (&bf)[8]) {
     const char* kr = st + (bi * 32 + r) * kIxKeyBytes;
@@ -352,10 +395,7 @@ __global__ __launch_bounds__(kIxThreads, 1) void indexer_topk_kernel(IxArgs a) {
   // Final selection and output (keys in increasing order, -1 / -inf after
   // the last selected one).
   if (w < nq) {
-    if (cnt > k) {
-      compact_candidates(cand_s, cand_i, cnt, k, hist, lane);
-      cnt = k;
-    }
+    if (cnt > k) compact_candidates<true>(cand_s, cand_i, cnt, k, hist, lane, cnt);
     const int64_t t = q0 + w;
     for (int i = lane; i < k; i += 64) {
       const bool have = i < cnt;
