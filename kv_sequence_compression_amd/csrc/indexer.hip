@@ -22,17 +22,22 @@
 // accumulator sets).
 //
 // Selection: each query owns a candidate buffer of 1536 (score, key) slots in
-// LDS and a threshold tau, the k-th best score seen so far (-inf until k
-// keys were kept).  A visible key whose score beats tau is appended (ballot
+// LDS and a threshold tau at or below the k-th best score seen so far (-inf
+// until the first compaction).  A visible key whose score beats tau is appended (ballot
 // + lane prefix counts; keys arrive in increasing order, so the buffer stays
-// sorted by key).  When a buffer could overflow within the next stage, the
-// wave finds the k-th best candidate by a radix select on order-preserving
-// 32-bit keys of the scores (4 passes of 8-bit histograms in LDS), keeps the
-// k best in place -- a stable compaction, so ties at the threshold go to the
-// smaller key index -- and raises tau to that score.  A later key with a
-// score equal to tau has a larger index and so ranks below every kept one:
-// the strict test "score > tau" is exact.  At the end of the sweep one more
-// compaction leaves the k best, listed by increasing key index.
+// sorted by key).  When any buffer of the tile could overflow within the
+// next stage, every wave compacts its buffer at the stage start (all at once,
+// so no wave waits at the next barrier for another's compaction).  A
+// compaction loads the candidates' order-preserving 32-bit keys into
+// registers and radix-selects the k-th best over the bits below their common
+// prefix (8-bit histograms in LDS).  Between stages one pass usually
+// suffices: the wave keeps every candidate at or above the lower edge of the
+// k-th best's bin (a stable compaction, at least the k best) and raises tau
+// to that edge.  A later key that only equals tau ranks below the k best
+// (either its score is lower or it ties with a smaller index), so the strict
+// test "score > tau" loses nothing.  At the end of the sweep an exact
+// selection (all passes, ties to the smaller key index) leaves the k best,
+// listed by increasing key index.
 //
 // Keys travel global -> LDS directly (buffer_load ... lds, 16 bytes a lane,
 // whole 128-byte lines), through a ring of 3 stages (48 KiB), two stages
