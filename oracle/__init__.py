@@ -13,12 +13,13 @@ Sources (web pages, cited by title and equation/table label):
   table tbl-attn-seqcomp-overlap.
 * "Ch 04 · CSA — 长上下文的快通道" -- section 3 (token-level compressor,
   the 12-token worked example) and section 4 (lightning indexer).
-* "Ch 05 · HCA — 长上下文的全景镜" -- section 2 (HCA compression formula) and
-  the section on partial RoPE.
+* "Ch 05 · HCA — 长上下文的全景镜" -- section 2 (HCA compression formula and
+  the dense attention over the entries), the section on partial RoPE and the
+  attention sink.
 * "混合压缩注意力双方案解析：CSA与HCA技术对比与选型指南" -- section 3
   (mixed-precision storage).
 
-Every function is pinned by ``tests/test_oracle_pins.py`` against facts that
+Every function is pinned (``tests/test_oracle_*pins.py``) against facts that
 do not come from the oracle itself (exact rational arithmetic, closed forms,
 the worked example, library routines for the special cases).  No function
 here is "parity unpinned".
@@ -51,4 +52,7 @@ from .rope_store import (  # noqa: F401
 from .indexer import (  # noqa: F401
     index_scores,
     top_k,
+)
+from .mqa import (  # noqa: F401
+    shared_kv_mqa,
 )
