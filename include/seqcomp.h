@@ -265,6 +265,42 @@ int seqcomp_indexer_topk(const void* q, const float* w, const void* keys, int64_
 /* Workspace bytes of seqcomp_indexer_topk; (size_t)-1 on malformed arguments. */
 size_t seqcomp_indexer_workspace_bytes(const int64_t* cu_q_host, int64_t batch);
 
+/*
+ * Dense shared-KV multi-query attention with an attention sink over
+ * compressed entries ("Ch 05 · HCA — 长上下文的全景镜": dense attention over
+ * every entry, and the attention sink; "Ch 04 · CSA — 长上下文的快通道",
+ * section 6: all heads share one KV).  For query t and head h:
+ *     alpha = Softmax(scale * q[t, h] . [k_sink, e_1, ..., e_n])
+ *     out[t, h] = alpha_sink * v_sink + sum_s alpha_s * e_s
+ * where e_1..e_n are the entries visible to t (each entry is key and value).
+ *   q        [T x 128 x 512] bf16, packed by sequence (cu_q).
+ *   kv       [N x 512] bf16 entries, packed by sequence (cu_k), e.g. the
+ *            HCA compressor's output.
+ *   cu_q, cu_k [batch + 1] int64, host and device copies (same values).
+ *   n_valid  [T] int32 (device) or NULL: query t sees the first n_valid[t]
+ *            entries of its sequence (clamped to [0, its entry count]);
+ *            NULL: all.
+ *   k_sink   [512] bf16 or NULL (no sink); v_sink [512] bf16 or NULL (zero
+ *            value); both shared by all heads.
+ *   scale    the logit scale (1/sqrt(512) in the standard form); finite.
+ *   out      [T x 128 x 512] of out_dtype (SEQCOMP_BF16 or SEQCOMP_F32).
+ *   lse      [T x 128] fp32 or NULL: natural log of the softmax denominator
+ *            of the scaled logits (sink included); -inf when nothing is
+ *            visible and there is no sink (then out is zero).
+ * Products are exact bf16 x bf16 in fp32; the probabilities are rounded to
+ * bf16 for the value product.  Requires n_heads == 128, head_dim == 512,
+ * bf16 q / kv / sink, and fewer than 2^21 entries per sequence.
+ *   workspace: seqcomp_mqa_workspace_bytes(cu_q_host, batch) bytes.
+ */
+int seqcomp_shared_kv_mqa(const void* q, const void* kv, int64_t n_heads, int64_t head_dim, int in_dtype,
+                          const int64_t* cu_q_host, const int64_t* cu_q_dev, const int64_t* cu_k_host,
+                          const int64_t* cu_k_dev, int64_t batch, const int32_t* n_valid, const void* k_sink,
+                          const void* v_sink, float scale, void* out, int out_dtype, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of seqcomp_shared_kv_mqa; (size_t)-1 on malformed arguments. */
+size_t seqcomp_mqa_workspace_bytes(const int64_t* cu_q_host, int64_t batch);
+
 #ifdef __cplusplus
 }
 #endif

@@ -292,3 +292,36 @@ def indexer_topk(q, w, keys, k: int, cu_q=None, cu_k=None, n_valid=None, with_sc
                                       _ptr(idx), _ptr(sc), _ptr(ws), ws_n, _stream(dev)),
            "seqcomp_indexer_topk")
     return idx, sc
+
+
+def shared_kv_mqa(q, kv, cu_q=None, cu_k=None, n_valid=None, k_sink=None, v_sink=None, scale=None,
+                  out_dtype: str = "bf16", with_lse: bool = False):
+    """Dense shared-KV multi-query attention with an attention sink:
+    out[t, h] = softmax(scale * q[t, h] . [k_sink, e_1..e_n]) . [v_sink, e_1..e_n]
+    over the entries e of t's sequence that t sees.  q [T x 128 x 512] bf16,
+    kv [N x 512] bf16 (entries are keys and values); cu_q / cu_k pack them by
+    sequence (default: one sequence); n_valid [T] int32 (default: all);
+    k_sink / v_sink [512] bf16 or None; scale defaults to 1/sqrt(512).
+    Returns (out [T x 128 x 512] of out_dtype, lse [T x 128] fp32 or None)."""
+    T = q.shape[0]
+    N = kv.shape[0]
+    dev = q.device
+    if q.dim() != 3 or kv.dim() != 2:
+        raise ValueError("q must be [T x H x D] and kv [N x D]")
+    hq, cq = _cu_arrays([0, T] if cu_q is None else cu_q, dev)
+    hk, ck = _cu_arrays([0, N] if cu_k is None else cu_k, dev)
+    if hq.size != hk.size:
+        raise ValueError("cu_q and cu_k must describe the same number of sequences")
+    nv = None if n_valid is None else torch.as_tensor(n_valid, dtype=torch.int32, device=dev).contiguous()
+    sc_ = float(scale) if scale is not None else 1.0 / float(np.sqrt(q.shape[2]))
+    out = torch.empty(tuple(q.shape), dtype=_TORCH_OUT[out_dtype], device=dev)
+    lse = torch.empty((T, q.shape[1]), dtype=torch.float32, device=dev) if with_lse else None
+    ws_n = lib().seqcomp_mqa_workspace_bytes(_i64p(hq), hq.size - 1)
+    if ws_n == ctypes.c_size_t(-1).value:
+        raise ValueError("malformed cu_q")
+    ws = _alloc_ws(ws_n, dev)
+    _check(lib().seqcomp_shared_kv_mqa(_ptr(q), _ptr(kv), q.shape[1], q.shape[2], _in_code(q), _i64p(hq), _ptr(cq),
+                                       _i64p(hk), _ptr(ck), hq.size - 1, _ptr(nv), _ptr(k_sink), _ptr(v_sink), sc_,
+                                       _ptr(out), _DT_CODE[out_dtype], _ptr(lse), _ptr(ws), ws_n, _stream(dev)),
+           "seqcomp_shared_kv_mqa")
+    return out, lse

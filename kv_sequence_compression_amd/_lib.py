@@ -45,6 +45,9 @@ SIGNATURES = {
     "seqcomp_indexer_topk": (_c_int, [_vp, _vp, _vp, _c_i64, _c_i64, _c_int, _i64p, _vp, _i64p, _vp, _c_i64,
                                       _vp, _c_i64, _vp, _vp, _vp, _size, _vp]),
     "seqcomp_indexer_workspace_bytes": (_size, [_i64p, _c_i64]),
+    "seqcomp_shared_kv_mqa": (_c_int, [_vp, _vp, _c_i64, _c_i64, _c_int, _i64p, _vp, _i64p, _vp, _c_i64, _vp, _vp,
+                                       _vp, ctypes.c_float, _vp, _c_int, _vp, _vp, _size, _vp]),
+    "seqcomp_mqa_workspace_bytes": (_size, [_i64p, _c_i64]),
 }
 
 _lib = None

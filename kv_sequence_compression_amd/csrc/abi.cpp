@@ -495,4 +495,58 @@ int seqcomp_indexer_topk(const void* q, const float* w, const void* keys, int64_
   return hip_status(e);
 }
 
+size_t seqcomp_mqa_workspace_bytes(const int64_t* cu_q_host, int64_t batch) {
+  int64_t T;
+  if (check_cu(cu_q_host, batch, &T) != SEQCOMP_OK) return (size_t)-1;
+  if (T == 0) return 0;
+  return round_up((size_t)T * sizeof(TileRec), 256);
+}
+
+int seqcomp_shared_kv_mqa(const void* q, const void* kv, int64_t n_heads, int64_t head_dim, int in_dtype,
+                          const int64_t* cu_q_host, const int64_t* cu_q_dev, const int64_t* cu_k_host,
+                          const int64_t* cu_k_dev, int64_t batch, const int32_t* n_valid, const void* k_sink,
+                          const void* v_sink, float scale, void* out, int out_dtype, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (in_dtype != SEQCOMP_BF16) return SEQCOMP_E_DTYPE;
+  if (out_dtype != SEQCOMP_BF16 && out_dtype != SEQCOMP_F32) return SEQCOMP_E_DTYPE;
+  if (n_heads != kMqaHeads || head_dim != kMqaDim) return SEQCOMP_E_UNSUPPORTED;
+  if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return SEQCOMP_E_SHAPE;   // NaN or infinite
+  int64_t T = 0, N = 0;
+  int st = check_cu(cu_q_host, batch, &T);
+  if (st) return st;
+  if ((st = check_cu(cu_k_host, batch, &N))) return st;
+  // entry offsets of a sequence stay below 2^31 bytes
+  for (int64_t b = 0; b < batch; ++b)
+    if (cu_k_host[b + 1] - cu_k_host[b] >= (int64_t(1) << 21)) return SEQCOMP_E_UNSUPPORTED;
+  if (T > (int64_t(1) << 30)) return SEQCOMP_E_UNSUPPORTED;                               // grid of 2 T
+  if (T == 0) return SEQCOMP_OK;
+  if (!q || !out || !cu_q_dev || !cu_k_dev || (N > 0 && !kv) || (v_sink && !k_sink)) return SEQCOMP_E_NULL;
+  if (!aligned16(q) || !aligned16(out) || (kv && !aligned16(kv)) || !aligned16(cu_q_dev) || !aligned16(cu_k_dev) ||
+      (k_sink && !aligned16(k_sink)) || (v_sink && !aligned16(v_sink)) || (lse && !aligned16(lse)) ||
+      (n_valid && (reinterpret_cast<uintptr_t>(n_valid) & 3u)))
+    return SEQCOMP_E_ALIGN;
+  const size_t need = seqcomp_mqa_workspace_bytes(cu_q_host, batch);
+  Range ws_r;
+  if ((st = check_workspace(workspace, workspace_bytes, need, &ws_r))) return st;
+  Range reads[7];
+  int nr = 0;
+  reads[nr++] = range_of(q, (size_t)T * kMqaHeads * kMqaDim * 2);
+  if (kv) reads[nr++] = range_of(kv, (size_t)N * kMqaDim * 2);
+  reads[nr++] = range_of(cu_q_dev, (size_t)(batch + 1) * 8);
+  reads[nr++] = range_of(cu_k_dev, (size_t)(batch + 1) * 8);
+  if (n_valid) reads[nr++] = range_of(n_valid, (size_t)T * 4);
+  if (k_sink) reads[nr++] = range_of(k_sink, kMqaDim * 2);
+  if (v_sink) reads[nr++] = range_of(v_sink, kMqaDim * 2);
+  const Range writes[3] = {range_of(out, (size_t)T * kMqaHeads * kMqaDim * elt_size(out_dtype)),
+                           lse ? range_of(lse, (size_t)T * kMqaHeads * 4) : Range(), ws_r};
+  if ((st = check_alias(writes, 3, reads, nr))) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TileRec* tiles = static_cast<TileRec*>(workspace);
+  hipError_t e = launch_plan(cu_q_dev, (int)batch, 1, 1, tiles, (int)T, s);
+  if (e == hipSuccess)
+    e = launch_mqa_sink(out_dtype == SEQCOMP_BF16 ? DT_BF16 : DT_F32, q, kv, cu_k_dev, n_valid, tiles, (int)T,
+                        k_sink, v_sink, scale, out, lse, s);
+  return hip_status(e);
+}
+
 }  // extern "C"

@@ -77,6 +77,15 @@ hipError_t launch_indexer_topk(const void* q, const float* w, const void* keys, 
                                const int32_t* n_valid, const TileRec* tiles, int n_tiles, int k, int32_t* out_idx,
                                float* out_score, hipStream_t stream);
 
+// Dense shared-KV MQA with an attention sink over compressed entries: 128
+// heads of 512 dims; one workgroup per query (tiles from the planner with
+// m = 1, tile_rows = 1).  out_dt is DT_BF16 or DT_F32.
+constexpr int kMqaHeads = 128;
+constexpr int kMqaDim = 512;
+hipError_t launch_mqa_sink(int out_dt, const void* q, const void* kv, const int64_t* cu_k_dev, const int32_t* n_valid,
+                           const TileRec* tiles, int T, const void* k_sink, const void* v_sink, float scale, void* out,
+                           float* lse, hipStream_t stream);
+
 hipError_t launch_csa_fixup(int out_dt, const TileRec* tiles, int n_tiles, int c, const float* halo,
                             void* out, hipStream_t stream);
 

@@ -1,0 +1,333 @@
+// Dense shared-KV multi-query attention with an attention sink, over the
+// compressed entries ("Ch 05 · HCA — 长上下文的全景镜": dense attention over all
+// n/m' entries, and the attention sink of its section 4; "Ch 04 · CSA —
+// 长上下文的快通道", section 6: the n_h = 128 heads share one KV).  For query t
+// and head h, over the entries s its sequence shows it (and the sink):
+//
+//     alpha = Softmax(scale * q[t, h] . [k_sink, e_1, ..., e_n])
+//     o[t, h] = alpha_sink * v_sink + sum_s alpha_s * e_s
+//
+// An entry serves as key and value; v_sink may be absent (zero).
+//
+// One workgroup takes 64 of a query's 128 heads (two workgroups per query):
+// those heads are the rows, and all of them share each tile of 64 entries
+// (64 KiB of bf16, staged global -> LDS, double-buffered).  Per tile, two
+// MFMA phases on v_mfma_f32_32x32x16_bf16:
+//  * scores: wave w forms the 32 x 32 block S^T = E Q^T of head block w & 1
+//    and entry block w >> 1 (A = entry fragments from LDS, B = the head
+//    block's query fragments, held in registers for the whole sweep).  Lane l
+//    then holds head l % 32 of the block and 16 of the 32 entries; one
+//    exchange between lanes l and l ^ 32 and one between the two waves that
+//    share a head block (through LDS) give the tile maximum per head.  The
+//    probabilities go to LDS as bf16, P[head][entry];
+//  * values: wave w accumulates O^T = E^T P^T for output columns
+//    128 w .. 128 w + 127 of the 64 heads (8 accumulators of 32 x 32).  The
+//    A operand needs 8 consecutive entries of one column per lane: the gfx950
+//    transposing LDS read (ds_read_b64_tr_b16) delivers them from the
+//    row-major entry tile, 4 entries per read.
+// The running maximum of a head is raised only when a tile's maximum exceeds
+// it by more than 8 (log2 units), so probabilities stay below 2^8 and the
+// accumulators are rescaled rarely.  The sink enters as the initial state:
+// maximum = its logit, sum = 1, accumulator = v_sink.
+//
+// LDS: entry tiles 2 x 64 KiB; 16-byte chunk c of entry row r at slot
+// c ^ f(r), f(r) = ((r & 3) << 2) | ((r >> 2) & 3): the score phase's reads
+// (one chunk of 16 consecutive rows) and the value phase's transposing reads
+// (two adjacent chunks of 4 consecutive rows) both touch distinct banks.
+// P: 64 rows of 128 bytes, chunk c of head row h at slot c ^ ((h >> 1) & 7).
+#include "amdgcn.hpp"
+#include "launch.hpp"
+
+namespace seqcomp {
+
+namespace {
+
+constexpr int kMqThreads = 256;
+constexpr int kMqTile = 64;                                   // entries per tile
+constexpr int kMqRowBytes = kMqaDim * 2;                      // 1 KiB per bf16 entry
+constexpr int kMqTileBytes = kMqTile * kMqRowBytes;           // 64 KiB
+constexpr int kMqHeadsPerWg = 64;                             // half of a query's heads
+constexpr int kMqPOff = 2 * kMqTileBytes;                     // P: 64 heads x 64 entries bf16
+constexpr int kMqMaxOff = kMqPOff + kMqHeadsPerWg * kMqTile * 2;   // per-head tile maxima, 2 halves
+constexpr int kMqSumOff = kMqMaxOff + 2 * kMqHeadsPerWg * 4;  // per-head tile sums, 2 halves
+constexpr int kMqFacOff = kMqSumOff + 2 * kMqHeadsPerWg * 4;  // per-head rescale factors
+constexpr int kMqInvOff = kMqFacOff + kMqHeadsPerWg * 4;      // per-head 1 / sum at the end
+constexpr int kMqFlagOff = kMqInvOff + kMqHeadsPerWg * 4;     // one rescale flag per wave
+constexpr int kMqLdsBytes = kMqFlagOff + 16;
+static_assert(kMqaHeads == 128 && kMqaDim == 512, "fragment layout assumes 128 heads of 512 dims");
+constexpr float kMqHeadroom = 8.f;                            // log2 growth allowed before a rescale
+
+struct MqArgs {
+  const char* q;            // [T][128][512] bf16
+  const char* kv;           // [N][512] bf16
+  const int64_t* cu_k;      // [batch + 1]
+  const int32_t* n_valid;   // [T] or null
+  const TileRec* tiles;     // one per query; workgroups 2 t and 2 t + 1 take its two head halves
+  const char* k_sink;       // [512] bf16 or null
+  const char* v_sink;       // [512] bf16 or null
+  float c2;                 // scale * log2(e)
+  char* out;                // [T][128][512] of out_dt
+  float* lse;               // [T][128] or null
+};
+
+__device__ __forceinline__ int kv_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+template <int DOUT>
+__global__ __launch_bounds__(kMqThreads, 1) void mqa_sink_kernel(MqArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds[kMqLdsBytes];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int h2 = lane >> 5;                 // lane half
+  const TileRec tile = a.tiles[blockIdx.x >> 1];
+  const int head0 = (blockIdx.x & 1) * kMqHeadsPerWg;
+  const int seq = tile_seq(tile.flags);
+  const int64_t t = tile.row_start;
+  const int64_t kbase = a.cu_k[seq];
+  const int nk = (int)(a.cu_k[seq + 1] - kbase);
+  const int nv = a.n_valid ? min(max(a.n_valid[t], 0), nk) : nk;
+  const int n_tiles = (nv + kMqTile - 1) / kMqTile;
+
+  // Score phase role: head block hb (32 heads), entry block kb (32 of the
+  // tile's 64 entries).  Query fragments of the head block: B operand of
+  // S^T = E Q^T; k-step kk covers dims 16 kk .. 16 kk + 15, lane half h2
+  // the 8 from 16 kk + 8 h2.
+  const int hb_s = w & 1, kb_s = w >> 1;
+  const int hl = 32 * hb_s + (lane & 31);   // head within the workgroup
+  bf16x8_t qf[32];
+  {
+    const char* qrow = a.q + ((t * kMqaHeads + head0 + hl) * kMqRowBytes) + h2 * 16;
+#pragma unroll
+    for (int kk = 0; kk < 32; ++kk) qf[kk] = __builtin_bit_cast(bf16x8_t, ld16(qrow + kk * 32));
+  }
+
+  // Online softmax state of head hl, kept alike by the two waves of its head
+  // block (and both lane halves).
+  float m_used = -INFINITY, l_run = 0.f;
+  if (a.k_sink) {
+    float dot = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 32; ++kk) {
+      const uint4 ks = ld16(a.k_sink + kk * 32 + h2 * 16);
+      const uint32_t kw[4] = {ks.x, ks.y, ks.z, ks.w};
+      const uint4 qv = __builtin_bit_cast(uint4, qf[kk]);
+      const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dot = fmaf(__uint_as_float(qw[e] << 16), __uint_as_float(kw[e] << 16), dot);
+        dot = fmaf(__uint_as_float(qw[e] & 0xffff0000u), __uint_as_float(kw[e] & 0xffff0000u), dot);
+      }
+    }
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(dot), __float_as_uint(dot), false, false);
+    dot = h2 ? __uint_as_float(sw[0]) + dot : dot + __uint_as_float(sw[1]);
+    m_used = dot * a.c2;
+    l_run = 1.f;
+  }
+
+  // Value phase role: output columns 128 w .. 128 w + 127 of the 64 heads.
+  // Accumulators O^T[cb][hb]: column 128 w + 32 cb + (8 g + 4 h2 + i), head
+  // 32 hb + l % 32 (element 4 g + i).  The sink's value is the start.
+  f32x16_t o[4][2];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    f32x16_t init = f32x16_t{};
+    if (a.k_sink && a.v_sink) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint2 v = *reinterpret_cast<const uint2*>(a.v_sink + (128 * w + 32 * cb + 8 * g + 4 * h2) * 2);
+        init[4 * g + 0] = __uint_as_float(v.x << 16);
+        init[4 * g + 1] = __uint_as_float(v.x & 0xffff0000u);
+        init[4 * g + 2] = __uint_as_float(v.y << 16);
+        init[4 * g + 3] = __uint_as_float(v.y & 0xffff0000u);
+      }
+    }
+    o[cb][0] = init;
+    o[cb][1] = init;
+  }
+
+  char* const P = lds + kMqPOff;
+  float* const pmax = reinterpret_cast<float*>(lds + kMqMaxOff);   // [kb][64]
+  float* const psm = reinterpret_cast<float*>(lds + kMqSumOff);    // [kb][64]
+  float* const fac = reinterpret_cast<float*>(lds + kMqFacOff);    // [64]
+  float* const inv = reinterpret_cast<float*>(lds + kMqInvOff);    // [64]
+  uint8_t* const flags = reinterpret_cast<uint8_t*>(lds + kMqFlagOff);
+
+  // Copies of one tile: wave w fills rows 16 w .. 16 w + 15, one 1 KiB row per
+  // copy; lane p writes slot p, which holds chunk p ^ f(row) of that entry.
+  const __amdgpu_buffer_rsrc_t src = ranged_rsrc(a.kv + kbase * kMqRowBytes, (uint32_t)nk * kMqRowBytes);
+  const auto issue_tile = [&](int j) {
+    char* dst = lds + (j & 1) * kMqTileBytes;
+    const uint32_t so = (uint32_t)j * kMqTileBytes;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 16 * w + i;
+      const uint32_t voff = (uint32_t)(r * kMqRowBytes + ((lane ^ kv_swz(i)) << 4)) + so;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)(dst + r * kMqRowBytes), 16, voff, 0, 0, 0);
+    }
+  };
+
+  const int r_s = 32 * kb_s + (lane & 31);                  // entry row of the score-phase A fragment
+  const int i16 = lane & 15, grp = (lane >> 4) & 1;
+  if (n_tiles > 0) issue_tile(0);
+#pragma unroll 1
+  for (int j = 0; j < n_tiles; ++j) {
+    wait_vmcnt_lgkm0<0>();            // tile j landed (own copies)
+    lds_barrier();                    // tile j visible; every wave is done with tile j - 1 and with P
+    if (j + 1 < n_tiles) issue_tile(j + 1);
+    const char* E = lds + (j & 1) * kMqTileBytes;
+
+    // ---- scores S^T[entry][head]: entries 32 kb_s .., heads 32 hb_s ..
+    f32x16_t s = f32x16_t{};
+    const char* erow = E + r_s * kMqRowBytes;
+    const int eswz = kv_swz(r_s);
+#pragma unroll
+    for (int kk = 0; kk < 32; ++kk) {
+      const f32x4_t ef = *reinterpret_cast<const f32x4_t*>(erow + (((2 * kk + h2) ^ eswz) << 4));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ef), qf[kk], s, 0, 0, 0);
+    }
+
+    // ---- online softmax of head hl over the tile (log2 units); the other
+    // 32 entries of the tile are the partner wave's (kb_s ^ 1)
+    const int e0 = j * kMqTile + 32 * kb_s;
+    float mt = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = e0 + 8 * (e >> 2) + 4 * h2 + (e & 3);
+      const float v = key < nv ? s[e] * a.c2 : -INFINITY;
+      s[e] = v;
+      mt = fmaxf(mt, v);
+    }
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+      mt = fmaxf(mt, __uint_as_float(h2 ? sw[0] : sw[1]));
+    }
+    if (h2 == 0) pmax[kb_s * 64 + hl] = mt;
+    wait_lgkmcnt0();
+    lds_barrier();                    // both halves' maxima are in
+    mt = fmaxf(mt, pmax[(kb_s ^ 1) * 64 + hl]);
+    const float m_new = mt > m_used + kMqHeadroom ? mt : m_used;
+    const float factor = m_new == m_used ? 1.f : exp2_hw(m_used - m_new);
+    const float ms = m_new == -INFINITY ? 0.f : m_new;
+    float psum = 0.f;
+    char* const prow = P + hl * 128;
+    const int pswz = (hl >> 1) & 7;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = exp2_hw(s[4 * g + i] - ms);
+        psum += p[i];
+      }
+      *reinterpret_cast<uint2*>(prow + (((4 * kb_s + g) ^ pswz) << 4) + 8 * h2) =
+          make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+    }
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(psum), __float_as_uint(psum), false, false);
+      psum = h2 ? __uint_as_float(sw[0]) + psum : psum + __uint_as_float(sw[1]);
+    }
+    if (h2 == 0) {
+      psm[kb_s * 64 + hl] = psum;
+      if (kb_s == 0) fac[hl] = factor;
+    }
+    m_used = m_new;
+    const bool rescale = __ballot(factor != 1.f) != 0;   // every lane votes, then lane 0 records it
+    if (lane == 0) flags[w] = rescale ? 1 : 0;
+    wait_lgkmcnt0();
+    lds_barrier();                    // P, sums, factors and flags of every head are in
+    l_run = l_run * factor + (psm[hl] + psm[64 + hl]);
+
+    // ---- values: O^T[col][head] += E^T[col][entry] P^T[entry][head]
+    if (*reinterpret_cast<const uint32_t*>(flags)) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const float f = fac[32 * hb + (lane & 31)];
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[cb][hb][e] *= f;
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {                  // 16 entries per step
+      bf16x8_t af[4], bfp[2];
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int col = 128 * w + 32 * cb + 16 * grp + 4 * (i16 & 3);
+        typedef short v4s __attribute__((ext_vector_type(4)));
+        v4s part[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int r = 16 * ks + 8 * h2 + 4 * half + (i16 >> 2);
+          const char* addr = E + r * kMqRowBytes + (((col >> 3) ^ kv_swz(r)) << 4) + ((col & 7) << 1);
+          part[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)addr);
+        }
+        const uint2 lo = __builtin_bit_cast(uint2, part[0]), hi = __builtin_bit_cast(uint2, part[1]);
+        af[cb] = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+      }
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const int hd = 32 * hb + (lane & 31);
+        bfp[hb] = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const uint4*>(P + hd * 128 + (((2 * ks + h2) ^ ((hd >> 1) & 7)) << 4)));
+      }
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+          o[cb][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cb], bfp[hb], o[cb][hb], 0, 0, 0);
+    }
+  }
+
+  // ---- normalise and store: o[t][head][col] = O^T[col][head] / sum
+  if (kb_s == 0 && h2 == 0) {
+    inv[hl] = l_run > 0.f ? 1.f / l_run : 0.f;
+    if (a.lse)
+      a.lse[t * kMqaHeads + head0 + hl] =
+          l_run > 0.f ? (m_used + __log2f(l_run)) * 0.6931471805599453f : -INFINITY;
+  }
+  wait_lgkmcnt0();
+  lds_barrier();
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const int hd = 32 * hb + (lane & 31);
+    const float f = inv[hd];
+    char* orow = a.out + (t * kMqaHeads + head0 + hd) * (int64_t)kMqaDim * (DOUT == DT_BF16 ? 2 : 4);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = 128 * w + 32 * cb + 8 * g + 4 * h2;
+        const float v0 = o[cb][hb][4 * g] * f, v1 = o[cb][hb][4 * g + 1] * f;
+        const float v2 = o[cb][hb][4 * g + 2] * f, v3 = o[cb][hb][4 * g + 3] * f;
+        if (DOUT == DT_BF16)
+          *reinterpret_cast<uint2*>(orow + col * 2) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+        else
+          *reinterpret_cast<float4*>(orow + col * 4) = make_float4(v0, v1, v2, v3);
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_mqa_sink(int out_dt, const void* q, const void* kv, const int64_t* cu_k_dev, const int32_t* n_valid,
+                           const TileRec* tiles, int T, const void* k_sink, const void* v_sink, float scale, void* out,
+                           float* lse, hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  MqArgs a;
+  a.q = static_cast<const char*>(q);
+  a.kv = static_cast<const char*>(kv);
+  a.cu_k = cu_k_dev;
+  a.n_valid = n_valid;
+  a.tiles = tiles;
+  a.k_sink = static_cast<const char*>(k_sink);
+  a.v_sink = static_cast<const char*>(v_sink);
+  a.c2 = scale * kLog2e;
+  a.out = static_cast<char*>(out);
+  a.lse = lse;
+  if (out_dt == DT_BF16)
+    hipLaunchKernelGGL(mqa_sink_kernel<DT_BF16>, dim3(2 * T), dim3(kMqThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(mqa_sink_kernel<DT_F32>, dim3(2 * T), dim3(kMqThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace seqcomp

@@ -22,7 +22,8 @@ m = 4 for CSA, m' = 128 for HCA, ~1M tokens):
 
 Tensor ids: H=1, W_KVa=2, W_KVb=3, W_Za=4, W_Zb=5, B^a=6, B^b=7, W_KV=8,
 W_Z=9, B=10, lengths=11, outlier channels=12, C^a=13, C^b=14, Z^a=15,
-Z^b=16, indexer queries q^I=17, head weights w^I=18, indexer keys=19.
+Z^b=16, indexer queries q^I=17, head weights w^I=18, indexer keys=19,
+attention queries=20, attended entries=21, sink key=22, sink value=23.
 
 Lightning-indexer inputs (64 heads of 128 dims, the pages' n_h^I and c^I):
 queries and keys bf16 N(0, 1), head weights fp32 N(0, 1) (learned weights
@@ -30,6 +31,11 @@ of either sign); or, for exact comparisons, small integers in [-3, 3] (every
 product and sum is then an integer well below 2^24, exact in fp32).  A query
 at position p of its sequence sees the compressed entries whose blocks of m
 tokens are complete, floor((p + 1) / m).
+
+Shared-KV attention inputs (128 heads of 512 dims, the pages' n_h and c):
+queries bf16 N(0, q_std^2), entries bf16 N(0, 1) (one vector per entry, key
+and value), sink key and value bf16 N(0, 1); the logit scale is 1/sqrt(512),
+so q_std sets how peaked the attention is.
 """
 
 from __future__ import annotations
@@ -40,7 +46,8 @@ import numpy as np
 import torch
 
 TID = dict(H=1, W_KVa=2, W_KVb=3, W_Za=4, W_Zb=5, Ba=6, Bb=7, W_KV=8, W_Z=9, B=10,
-           lengths=11, outliers=12, Ca=13, Cb=14, Za=15, Zb=16, Qidx=17, Widx=18, Kidx=19)
+           lengths=11, outliers=12, Ca=13, Cb=14, Za=15, Zb=16, Qidx=17, Widx=18, Kidx=19,
+           Qatt=20, KVatt=21, Ksink=22, Vsink=23)
 
 _TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -228,6 +235,10 @@ CONFIGS = {
     # compressed indexer keys (m = 4); its last 4096 tokens query them
     # (causal: floor((p + 1) / 4) visible), k = 1024.
     "indexer_1m": dict(kind="indexer", n_tokens=1 << 20, m=4, n_queries=4096, k=1024),
+    # HCA dense attention at 1M context: 2^20 tokens -> 8192 HCA entries
+    # (m' = 128); the last 4096 tokens attend (causal: floor((p + 1) / 128)
+    # visible), 128 heads x 512, with an attention sink; bf16 out.
+    "hca_mqa_1m": dict(kind="mqa", n_tokens=1 << 20, m=128, n_queries=4096, q_std=1.0),
 }
 
 
@@ -278,3 +289,28 @@ def indexer_case(q_lengths, k_lengths, *, seed: int = 0, device="cpu", integer: 
 def causal_visible(positions, m: int) -> np.ndarray:
     """Entries visible to queries at `positions`: complete blocks of m tokens."""
     return ((np.asarray(positions, dtype=np.int64) + 1) // m).astype(np.int32)
+
+
+MQA_HEADS = 128        # n_h
+MQA_DIM = 512          # c
+
+
+@dataclass
+class MqaCase:
+    q: torch.Tensor            # [T x 128 x 512] bf16
+    kv: torch.Tensor           # [N x 512] bf16
+    k_sink: torch.Tensor       # [512] bf16
+    v_sink: torch.Tensor       # [512] bf16
+    cu_q: np.ndarray
+    cu_k: np.ndarray
+
+
+def mqa_case(q_lengths, k_lengths, *, seed: int = 0, device="cpu", q_std: float = 1.0) -> MqaCase:
+    """Queries, entries and a sink for shared-KV attention over a packed batch:
+    sequence b has q_lengths[b] queries and k_lengths[b] entries."""
+    T, N = int(np.sum(q_lengths)), int(np.sum(k_lengths))
+    q = normal((T, MQA_HEADS, MQA_DIM), q_std, (seed, TID["Qatt"]), device, "bf16")
+    kv = normal((N, MQA_DIM), 1.0, (seed, TID["KVatt"]), device, "bf16")
+    ks = normal((MQA_DIM,), 1.0, (seed, TID["Ksink"]), device, "bf16")
+    vs = normal((MQA_DIM,), 1.0, (seed, TID["Vsink"]), device, "bf16")
+    return MqaCase(q, kv, ks, vs, cu_from_lengths(q_lengths), cu_from_lengths(k_lengths))

@@ -117,3 +117,40 @@ def check_topk_valid(idx, sc, I, nv, k, beta):
             s = set(sel.tolist())
             assert all(int(x) in s for x in must), t
             assert not any(int(x) in s for x in never), t
+
+
+# ------------------------------------------------- shared-KV attention checks
+
+def mqa_abs_weighted(Q, KV, nv, scale, k_sink=None, v_sink=None):
+    """sum_s alpha_s |v_s| per output element (float64), the scale of the
+    error the bf16 rounding of the probabilities can cause."""
+    absv = np.abs(KV)
+    vs = None if v_sink is None else np.abs(v_sink)
+    T, H, c = Q.shape
+    out = np.zeros((T, H, c))
+    for t in range(T):
+        K = KV[: int(nv[t])]
+        V = absv[: int(nv[t])]
+        if k_sink is not None:
+            K = np.vstack([k_sink[None], K])
+            V = np.vstack([(np.zeros(c) if v_sink is None else vs)[None], V])
+        if K.shape[0] == 0:
+            continue
+        lg = scale * (Q[t] @ K.T)
+        e = np.exp(lg - lg.max(1, keepdims=True))
+        out[t] = (e / e.sum(1, keepdims=True)) @ V
+    return out
+
+
+def check_mqa(out, ref, absw, out_dtype, lse=None, ref_lse=None):
+    """|gpu - ref| <= 2^-7 sum_s alpha_s |v_s| (+ 2^-8 |ref| for bf16 output):
+    each probability is rounded to bf16 (relative 2^-9) before the value
+    product, with a 4x margin; the log-sum-exp within 1e-4 absolute."""
+    tol = 2.0 ** -7 * absw + (2.0 ** -8 * np.abs(ref) if out_dtype == "bf16" else 0.0) + 1e-6
+    err = np.abs(out - ref)
+    assert np.all(err <= tol), f"max excess {np.max(err - tol)} at {np.unravel_index(np.argmax(err - tol), err.shape)}"
+    if lse is not None:
+        both_inf = np.isneginf(lse) & np.isneginf(ref_lse)
+        with np.errstate(invalid="ignore"):                  # -inf - -inf where nothing is visible
+            close = np.abs(lse - ref_lse) <= 1e-4
+        assert np.all(both_inf | close), np.nanmax(np.where(both_inf, 0.0, np.abs(lse - ref_lse)))

@@ -306,3 +306,53 @@ def test_indexer_empty_calls_launch_nothing(lib):
     # no queries: OK before any pointer is looked at; keys may be absent when there are none
     assert indexer(lib, cu_q=_cu(0, 0), q=0, w=0, idx=0, sc=0, ws=0, ws_bytes=0) == S["SEQCOMP_OK"]
     assert indexer(lib, cu_k=_cu(0, 0), keys=0, cu_q=_cu(0, 0), q=0, w=0, idx=0, ws=0) == S["SEQCOMP_OK"]
+
+
+KSINK, VSINK, LSE = 0x50400000, 0x50500000, 0x90000000
+
+
+def mqa(lib, **kw):
+    a = dict(q=A, kv=C_, H=128, D=512, in_dt=_lib.BF16, cu_q=_cu(0, 4096), cu_q_dev=CU_DEV, cu_k=_cu(0, 8192),
+             cu_k_dev=CU_K_DEV, nv=D_, ks=KSINK, vs=VSINK, scale=0.044, out=OUT, out_dt=_lib.BF16, lse=LSE, ws=WS,
+             ws_bytes=1 << 20)
+    a.update(kw)
+    cq, ck = a["cu_q"], a["cu_k"]
+    return lib.seqcomp_shared_kv_mqa(a["q"], a["kv"], a["H"], a["D"], a["in_dt"], _p(cq), a["cu_q_dev"], _p(ck),
+                                     a["cu_k_dev"], cq.size - 1, a["nv"], a["ks"], a["vs"], a["scale"], a["out"],
+                                     a["out_dt"], a["lse"], a["ws"], a["ws_bytes"], None)
+
+
+def test_mqa_workspace(lib):
+    f = lib.seqcomp_mqa_workspace_bytes
+    assert f(_p(_cu(0, 4096)), 1) == 4096 * 16         # one tile record per query
+    assert f(_p(_cu(0, 3, 3, 5)), 3) == 256
+    assert f(_p(_cu(0, 0)), 1) == 0
+    assert f(_p(_cu(2, 5)), 1) == ctypes.c_size_t(-1).value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(in_dt=_lib.F32), "SEQCOMP_E_DTYPE"),
+    (dict(out_dt=_lib.FP8_E4M3), "SEQCOMP_E_DTYPE"),
+    (dict(H=64), "SEQCOMP_E_UNSUPPORTED"),
+    (dict(D=128), "SEQCOMP_E_UNSUPPORTED"),
+    (dict(scale=float("nan")), "SEQCOMP_E_SHAPE"),
+    (dict(scale=float("inf")), "SEQCOMP_E_SHAPE"),
+    (dict(cu_k=_cu(0, 1 << 21)), "SEQCOMP_E_UNSUPPORTED"),     # entry offsets must stay below 2^31 bytes
+    (dict(cu_q=_cu(0, 5, 4), cu_k=_cu(0, 5, 9)), "SEQCOMP_E_SEQLENS"),
+    (dict(q=0), "SEQCOMP_E_NULL"),
+    (dict(kv=0), "SEQCOMP_E_NULL"),
+    (dict(out=0), "SEQCOMP_E_NULL"),
+    (dict(ks=0), "SEQCOMP_E_NULL"),                             # a sink value needs a sink key
+    (dict(vs=VSINK + 4), "SEQCOMP_E_ALIGN"),
+    (dict(nv=D_ + 2), "SEQCOMP_E_ALIGN"),
+    (dict(ws_bytes=64), "SEQCOMP_E_WORKSPACE"),
+    (dict(out=A + 4096), "SEQCOMP_E_ALIAS"),                     # output over the queries
+    (dict(lse=OUT + 4096), "SEQCOMP_E_ALIAS"),                   # log-sum-exp over the output
+    (dict(ws=C_ + 1024), "SEQCOMP_E_ALIAS"),                     # workspace over the entries
+])
+def test_mqa_rejects_bad_arguments(lib, kw, code):
+    assert mqa(lib, **kw) == S[code]
+
+
+def test_mqa_empty_calls_launch_nothing(lib):
+    assert mqa(lib, cu_q=_cu(0, 0), q=0, out=0, lse=0, ws=0, ws_bytes=0) == S["SEQCOMP_OK"]
