@@ -153,25 +153,25 @@ __global__ __launch_bounds__(kMqThreads, 1) void mqa_sink_kernel(MqArgs a) {
   // Copies of one tile: wave w fills rows 16 w .. 16 w + 15, one 1 KiB row per
   // copy; lane p writes slot p, which holds chunk p ^ f(row) of that entry.
   const __amdgpu_buffer_rsrc_t src = ranged_rsrc(a.kv + kbase * kMqRowBytes, (uint32_t)nk * kMqRowBytes);
-  const auto issue_tile = [&](int j) {
-    char* dst = lds + (j & 1) * kMqTileBytes;
-    const uint32_t so = (uint32_t)j * kMqTileBytes;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = 16 * w + i;
-      const uint32_t voff = (uint32_t)(r * kMqRowBytes + ((lane ^ kv_swz(i)) << 4)) + so;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)(dst + r * kMqRowBytes), 16, voff, 0, 0, 0);
-    }
+  // Each copy holds the issuing wave for ~16 cycles, so the next tile's copies
+  // are spread over the score MFMAs (one after every second), in their shadow.
+  const auto issue_row = [&](int j, int i) {
+    const int r = 16 * w + i;
+    const uint32_t voff = (uint32_t)(r * kMqRowBytes + ((lane ^ kv_swz(i)) << 4)) + (uint32_t)j * kMqTileBytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)(lds + (j & 1) * kMqTileBytes + r * kMqRowBytes), 16,
+                                             voff, 0, 0, 0);
   };
 
   const int r_s = 32 * kb_s + (lane & 31);                  // entry row of the score-phase A fragment
   const int i16 = lane & 15, grp = (lane >> 4) & 1;
-  if (n_tiles > 0) issue_tile(0);
+  if (n_tiles > 0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) issue_row(0, i);
+  }
 #pragma unroll 1
   for (int j = 0; j < n_tiles; ++j) {
     wait_vmcnt_lgkm0<0>();            // tile j landed (own copies)
     lds_barrier();                    // tile j visible; every wave is done with tile j - 1 and with P
-    if (j + 1 < n_tiles) issue_tile(j + 1);
     const char* E = lds + (j & 1) * kMqTileBytes;
 
     // ---- scores S^T[entry][head]: entries 32 kb_s .., heads 32 hb_s ..
@@ -182,6 +182,9 @@ __global__ __launch_bounds__(kMqThreads, 1) void mqa_sink_kernel(MqArgs a) {
     for (int kk = 0; kk < 32; ++kk) {
       const f32x4_t ef = *reinterpret_cast<const f32x4_t*>(erow + (((2 * kk + h2) ^ eswz) << 4));
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ef), qf[kk], s, 0, 0, 0);
+      // tile j + 1 (past the last tile: beyond the visible entries, where
+      // the descriptor's range returns zeros or the rows are never read)
+      if (kk & 1) issue_row(j + 1, kk >> 1);
     }
 
     // ---- online softmax of head hl over the tile (log2 units); the other
@@ -277,6 +280,7 @@ __global__ __launch_bounds__(kMqThreads, 1) void mqa_sink_kernel(MqArgs a) {
     }
   }
 
+  wait_vmcnt<0>();                    // no copy into this workgroup's LDS outlives it
   // ---- normalise and store: o[t][head][col] = O^T[col][head] / sum
   if (kb_s == 0 && h2 == 0) {
     inv[hl] = l_run > 0.f ? 1.f / l_run : 0.f;
