@@ -234,6 +234,53 @@ def lightning_indexer(sc, synth, torch, steps, cpu_queries=2):
     return res
 
 
+def hca_attention(sc, synth, torch, steps, cpu_queries=2):
+    """Dense shared-KV MQA with an attention sink over the HCA entries at 1M
+    context: 8192 entries (2^20 tokens, m' = 128), the sequence's last 4096
+    tokens as queries (causal visibility), 128 heads x 512 bf16, bf16 out.
+    MFMA-bound: 4 * 128 * 512 flops per visible (query, entry) pair (scores
+    and values)."""
+    cfg = synth.CONFIGS["hca_mqa_1m"]
+    n_tok, T, m = cfg["n_tokens"], cfg["n_queries"], cfg["m"]
+    dev = torch.device("cuda:0")
+    case = synth.mqa_case([T], [n_tok // m], seed=0, device=dev, q_std=cfg["q_std"])
+    nv = synth.causal_visible(np.arange(n_tok - T, n_tok), m)
+    pairs = float(nv.astype(np.float64).sum())
+    flops = 4.0 * synth.MQA_HEADS * synth.MQA_DIM * pairs
+    call = lambda: sc.shared_kv_mqa(case.q, case.kv, case.cu_q, case.cu_k, nv, case.k_sink, case.v_sink, None,
+                                    "bf16")
+    call()
+    torch.cuda.synchronize()
+    ev = _events(torch, 2)
+    ev[0].record()
+    for _ in range(steps):
+        call()
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    tf = flops / (ms * 1e-3) / 1e12
+    res = {"workload": f"hca_mqa_1m: {n_tok // m} entries (n={n_tok}, m'={m}), the last {T} tokens attend with "
+                       "causal visibility, 128 heads x 512 bf16, attention sink with value, bf16 out",
+           "flops_per_call": flops, "ms": ms, "queries_per_s": T / (ms * 1e-3), "tflops": tf,
+           "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": tf / PEAK_BF16_TFLOPS, "traffic": _traffic("hca_mqa_1m"),
+                        "kernel": "attention call (planner + mqa_sink_kernel)"}}
+    import oracle
+    rows = np.arange(T - cpu_queries, T)
+    Q = case.q[-cpu_queries:].double().cpu().numpy()
+    KV = case.kv.double().cpu().numpy()
+    ks = case.k_sink.double().cpu().numpy()
+    vs = case.v_sink.double().cpu().numpy()
+    t0 = time.perf_counter()
+    oracle.shared_kv_mqa(Q, KV, nv[rows], 1.0 / np.sqrt(synth.MQA_DIM), ks, vs)
+    dt = time.perf_counter() - t0
+    res["cpu_oracle"] = {"queries_per_s": cpu_queries / dt, "sample": f"{cpu_queries} queries x {n_tok // m} entries",
+                         "cores": _blas_threads(), "kind": "oracle"}
+    del case
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -244,8 +291,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-pool", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the indexer-key compressor, decode-append, RoPE-store and lightning-indexer "
-                         "measurements")
+                    help="skip the indexer-key compressor, decode-append, RoPE-store, lightning-indexer and "
+                         "HCA-attention measurements")
     ap.add_argument("--profile-copy", action="store_true",
                     help="first run a plain 1 GiB device copy (torch copy kernel): the known-size reference that "
                          "scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -372,6 +419,8 @@ def main():
         _progress("RoPE store measured")
         out["lightning_indexer"] = lightning_indexer(sc, synth, torch, args.steps)
         _progress("lightning indexer measured")
+        out["hca_attention"] = hca_attention(sc, synth, torch, args.steps)
+        _progress("HCA attention measured")
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(csa, hca, args.cpu_sample_tokens)
