@@ -25,10 +25,13 @@
 //    A operand needs 8 consecutive entries of one column per lane: the gfx950
 //    transposing LDS read (ds_read_b64_tr_b16) delivers them from the
 //    row-major entry tile, 4 entries per read.
-// The running maximum of a head is raised only when a tile's maximum exceeds
-// it by more than 8 (log2 units), so probabilities stay below 2^8 and the
-// accumulators are rescaled rarely.  The sink enters as the initial state:
-// maximum = its logit, sum = 1, accumulator = v_sink.
+// The softmax of a head is taken against a fixed reference: the larger of the
+// sink's logit and the first tile's maximum.  Later tiles may exceed it by up
+// to 64 (log2 units), so the accumulators are never rescaled; a tile that
+// exceeds it by more raises the reference and starts the sweep again (each
+// such restart moves past the tile that caused it, so there are at most as
+// many as tiles).  The sink joins the first tile's value phase as one more
+// entry, of key k_sink and value v_sink (or zero).
 //
 // LDS: entry tiles 2 x 64 KiB; 16-byte chunk c of entry row r at slot
 // c ^ f(r), f(r) = ((r & 3) << 2) | ((r >> 2) & 3): the score phase's reads
@@ -50,12 +53,12 @@ constexpr int kMqHeadsPerWg = 64;                             // half of a query
 constexpr int kMqPOff = 2 * kMqTileBytes;                     // P: 64 heads x 64 entries bf16
 constexpr int kMqMaxOff = kMqPOff + kMqHeadsPerWg * kMqTile * 2;   // per-head tile maxima, 2 halves
 constexpr int kMqSumOff = kMqMaxOff + 2 * kMqHeadsPerWg * 4;  // per-head tile sums, 2 halves
-constexpr int kMqFacOff = kMqSumOff + 2 * kMqHeadsPerWg * 4;  // per-head rescale factors
+constexpr int kMqFacOff = kMqSumOff + 2 * kMqHeadsPerWg * 4;  // per-head sink weights
 constexpr int kMqInvOff = kMqFacOff + kMqHeadsPerWg * 4;      // per-head 1 / sum at the end
-constexpr int kMqFlagOff = kMqInvOff + kMqHeadsPerWg * 4;     // one rescale flag per wave
+constexpr int kMqFlagOff = kMqInvOff + kMqHeadsPerWg * 4;     // one restart vote per wave
 constexpr int kMqLdsBytes = kMqFlagOff + 16;
 static_assert(kMqaHeads == 128 && kMqaDim == 512, "fragment layout assumes 128 heads of 512 dims");
-constexpr float kMqHeadroom = 8.f;                            // log2 growth allowed before a rescale
+constexpr float kMqHeadroom = 64.f;                           // log2 growth past the reference before a restart
 
 struct MqArgs {
   const char* q;            // [T][128][512] bf16
@@ -99,9 +102,8 @@ __global__ __launch_bounds__(kMqThreads, 1) void mqa_sink_kernel(MqArgs a) {
     for (int kk = 0; kk < 32; ++kk) qf[kk] = __builtin_bit_cast(bf16x8_t, ld16(qrow + kk * 32));
   }
 
-  // Online softmax state of head hl, kept alike by the two waves of its head
-  // block (and both lane halves).
-  float m_used = -INFINITY, l_run = 0.f;
+  // Sink logit of head hl (log2 units; -inf without a sink).
+  float s_sink = -INFINITY;
   if (a.k_sink) {
     float dot = 0.f;
 #pragma unroll
@@ -118,194 +120,234 @@ __global__ __launch_bounds__(kMqThreads, 1) void mqa_sink_kernel(MqArgs a) {
     }
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(dot), __float_as_uint(dot), false, false);
     dot = h2 ? __uint_as_float(sw[0]) + dot : dot + __uint_as_float(sw[1]);
-    m_used = dot * a.c2;
-    l_run = 1.f;
+    s_sink = dot * a.c2;
   }
+
+  // Softmax state of head hl, kept alike by the two waves of its head block
+  // (and both lane halves): the reference m_ref and the sum of
+  // 2^(logit - m_ref) over the entries.  m_ref is set at the first tile,
+  // before anything is accumulated, to the largest of the sink logit, that
+  // tile's maximum and the floor left by a restart; a later tile may exceed
+  // it by up to the headroom (2^64 fits bf16 and, times the values, fp32).  A
+  // tile that exceeds it by more ends the pass: the floor rises to that
+  // tile's maximum and the sweep starts again (never in practice: logits
+  // would have to grow by 44 natural units), so the accumulators are never
+  // rescaled.
+  float m_ref = -INFINITY, l_run = 0.f, m_floor = -INFINITY;
 
   // Value phase role: output columns 128 w .. 128 w + 127 of the 64 heads.
   // Accumulators O^T[cb][hb]: column 128 w + 32 cb + (8 g + 4 h2 + i), head
-  // 32 hb + l % 32 (element 4 g + i).  The sink's value is the start.
+  // 32 hb + l % 32 (element 4 g + i).  The sink's value joins at the end, as
+  // its weight times v_sink.
   f32x16_t o[4][2];
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
-    f32x16_t init = f32x16_t{};
-    if (a.k_sink && a.v_sink) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const uint2 v = *reinterpret_cast<const uint2*>(a.v_sink + (128 * w + 32 * cb + 8 * g + 4 * h2) * 2);
-        init[4 * g + 0] = __uint_as_float(v.x << 16);
-        init[4 * g + 1] = __uint_as_float(v.x & 0xffff0000u);
-        init[4 * g + 2] = __uint_as_float(v.y << 16);
-        init[4 * g + 3] = __uint_as_float(v.y & 0xffff0000u);
-      }
-    }
-    o[cb][0] = init;
-    o[cb][1] = init;
-  }
 
   char* const P = lds + kMqPOff;
   float* const pmax = reinterpret_cast<float*>(lds + kMqMaxOff);   // [kb][64]
   float* const psm = reinterpret_cast<float*>(lds + kMqSumOff);    // [kb][64]
-  float* const fac = reinterpret_cast<float*>(lds + kMqFacOff);    // [64]
+  float* const sinkw = reinterpret_cast<float*>(lds + kMqFacOff);  // [64] sink weight / sum at the end
   float* const inv = reinterpret_cast<float*>(lds + kMqInvOff);    // [64]
   uint8_t* const flags = reinterpret_cast<uint8_t*>(lds + kMqFlagOff);
 
   // Copies of one tile: wave w fills rows 16 w .. 16 w + 15, one 1 KiB row per
   // copy; lane p writes slot p, which holds chunk p ^ f(row) of that entry.
+  // The whole offset travels in the lane's offset register, the one part of
+  // the address that the descriptor's range check covers: rows past the
+  // sequence's entries then read as zeros.  Its row and tile part is a
+  // scalar (wave index through readfirstlane).
   const __amdgpu_buffer_rsrc_t src = ranged_rsrc(a.kv + kbase * kMqRowBytes, (uint32_t)nk * kMqRowBytes);
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   // Each copy holds the issuing wave for ~16 cycles, so the next tile's copies
   // are spread over the score MFMAs (one after every second), in their shadow.
-  const auto issue_row = [&](int j, int i) {
-    const int r = 16 * w + i;
-    const uint32_t voff = (uint32_t)(r * kMqRowBytes + ((lane ^ kv_swz(i)) << 4)) + (uint32_t)j * kMqTileBytes;
+  const auto issue_row = [&](int j, int i, int lane_v) {
+    const int r = 16 * wu + i;
+    const uint32_t row_off = (uint32_t)(r * kMqRowBytes) + (uint32_t)j * kMqTileBytes;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)(lds + (j & 1) * kMqTileBytes + r * kMqRowBytes), 16,
-                                             voff, 0, 0, 0);
+                                             (uint32_t)((lane_v ^ kv_swz(i)) << 4) + row_off, 0, 0, 0);
   };
 
+  // Per-lane offsets within a tile buffer (the rest are immediates):
+  //  * score A fragment, k-step kk = 8 m + u: row r_s, chunk (2 kk + h2) ^ f(r_s)
+  //    = 16 m + ((2 u + h2) ^ f(r_s)), i.e. koff[u] + 256 m;
+  //  * value A fragment, step ks, block cb, half: row 16 ks + 8 h2 + 4 half +
+  //    i16 / 4, column 128 w + 32 cb + 16 grp + 4 (i16 % 4): troff[half][cb] +
+  //    16 KiB ks (the swizzle depends on the row only through row % 16);
+  //  * P fragment of step ks: head row 32 hb + l % 32, chunk (2 ks + h2) ^ ps:
+  //    poff[ks] + 4 KiB hb.
   const int r_s = 32 * kb_s + (lane & 31);                  // entry row of the score-phase A fragment
   const int i16 = lane & 15, grp = (lane >> 4) & 1;
-  if (n_tiles > 0) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) issue_row(0, i);
-  }
-#pragma unroll 1
-  for (int j = 0; j < n_tiles; ++j) {
-    wait_vmcnt_lgkm0<0>();            // tile j landed (own copies)
-    lds_barrier();                    // tile j visible; every wave is done with tile j - 1 and with P
-    const char* E = lds + (j & 1) * kMqTileBytes;
-
-    // ---- scores S^T[entry][head]: entries 32 kb_s .., heads 32 hb_s ..
-    f32x16_t s = f32x16_t{};
-    const char* erow = E + r_s * kMqRowBytes;
+  uint32_t koff[8], troff[2][4], poff[4];
+  {
     const int eswz = kv_swz(r_s);
 #pragma unroll
-    for (int kk = 0; kk < 32; ++kk) {
-      const f32x4_t ef = *reinterpret_cast<const f32x4_t*>(erow + (((2 * kk + h2) ^ eswz) << 4));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ef), qf[kk], s, 0, 0, 0);
-      // tile j + 1 (past the last tile: beyond the visible entries, where
-      // the descriptor's range returns zeros or the rows are never read)
-      if (kk & 1) issue_row(j + 1, kk >> 1);
-    }
-
-    // ---- online softmax of head hl over the tile (log2 units); the other
-    // 32 entries of the tile are the partner wave's (kb_s ^ 1)
-    const int e0 = j * kMqTile + 32 * kb_s;
-    float mt = -INFINITY;
+    for (int u = 0; u < 8; ++u) koff[u] = (uint32_t)(r_s * kMqRowBytes + (((2 * u + h2) ^ eswz) << 4));
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int key = e0 + 8 * (e >> 2) + 4 * h2 + (e & 3);
-      const float v = key < nv ? s[e] * a.c2 : -INFINITY;
-      s[e] = v;
-      mt = fmaxf(mt, v);
-    }
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
-      mt = fmaxf(mt, __uint_as_float(h2 ? sw[0] : sw[1]));
-    }
-    if (h2 == 0) pmax[kb_s * 64 + hl] = mt;
-    wait_lgkmcnt0();
-    lds_barrier();                    // both halves' maxima are in
-    mt = fmaxf(mt, pmax[(kb_s ^ 1) * 64 + hl]);
-    const float m_new = mt > m_used + kMqHeadroom ? mt : m_used;
-    const float factor = m_new == m_used ? 1.f : exp2_hw(m_used - m_new);
-    const float ms = m_new == -INFINITY ? 0.f : m_new;
-    float psum = 0.f;
-    char* const prow = P + hl * 128;
-    const int pswz = (hl >> 1) & 7;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      float p[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = exp2_hw(s[4 * g + i] - ms);
-        psum += p[i];
-      }
-      *reinterpret_cast<uint2*>(prow + (((4 * kb_s + g) ^ pswz) << 4) + 8 * h2) =
-          make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
-    }
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(psum), __float_as_uint(psum), false, false);
-      psum = h2 ? __uint_as_float(sw[0]) + psum : psum + __uint_as_float(sw[1]);
-    }
-    if (h2 == 0) {
-      psm[kb_s * 64 + hl] = psum;
-      if (kb_s == 0) fac[hl] = factor;
-    }
-    m_used = m_new;
-    const bool rescale = __ballot(factor != 1.f) != 0;   // every lane votes, then lane 0 records it
-    if (lane == 0) flags[w] = rescale ? 1 : 0;
-    wait_lgkmcnt0();
-    lds_barrier();                    // P, sums, factors and flags of every head are in
-    l_run = l_run * factor + (psm[hl] + psm[64 + hl]);
-
-    // ---- values: O^T[col][head] += E^T[col][entry] P^T[entry][head]
-    if (*reinterpret_cast<const uint32_t*>(flags)) {
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        const float f = fac[32 * hb + (lane & 31)];
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) o[cb][hb][e] *= f;
-      }
-    }
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {                  // 16 entries per step
-      bf16x8_t af[4], bfp[2];
+    for (int half = 0; half < 2; ++half) {
+      const int r = 8 * h2 + 4 * half + (i16 >> 2);
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
         const int col = 128 * w + 32 * cb + 16 * grp + 4 * (i16 & 3);
-        typedef short v4s __attribute__((ext_vector_type(4)));
-        v4s part[2];
+        troff[half][cb] = (uint32_t)(r * kMqRowBytes + (((col >> 3) ^ kv_swz(r)) << 4) + ((col & 7) << 1));
+      }
+    }
+    const int ps = ((lane & 31) >> 1) & 7;
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int r = 16 * ks + 8 * h2 + 4 * half + (i16 >> 2);
-          const char* addr = E + r * kMqRowBytes + (((col >> 3) ^ kv_swz(r)) << 4) + ((col & 7) << 1);
-          part[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)addr);
+    for (int ks = 0; ks < 4; ++ks) poff[ks] = (uint32_t)((lane & 31) * 128 + (((2 * ks + h2) ^ ps) << 4));
+  }
+
+#pragma unroll 1
+  for (;;) {                          // one pass; a second only after a restart
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) o[cb][0] = o[cb][1] = f32x16_t{};
+    l_run = 0.f;
+    if (n_tiles > 0) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) issue_row(0, i, lane);
+    }
+    bool again = false;
+#pragma unroll 1
+    for (int j = 0; j < n_tiles; ++j) {
+      wait_vmcnt_lgkm0<0>();            // tile j landed (own copies)
+      lds_barrier();                    // tile j visible; every wave is done with tile j - 1 and with P
+      const char* E = lds + (j & 1) * kMqTileBytes;
+      int lane_v = lane;                // recomputed copy offsets: kept out of registers across tiles
+      asm volatile("" : "+v"(lane_v));
+
+      // ---- scores S^T[entry][head]: entries 32 kb_s .., heads 32 hb_s ..
+      f32x16_t s = f32x16_t{};
+#pragma unroll
+      for (int kk = 0; kk < 32; ++kk) {
+        const f32x4_t ef = *reinterpret_cast<const f32x4_t*>(E + koff[kk & 7] + 256 * (kk >> 3));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ef), qf[kk], s, 0, 0, 0);
+        // tile j + 1 (past the last tile: beyond the visible entries, where
+        // the descriptor's range returns zeros or the rows are never read)
+        if (kk & 1) issue_row(j + 1, kk >> 1, lane_v);
+      }
+
+      // ---- softmax of head hl over the tile (log2 units); the other 32
+      // entries of the tile are the partner wave's (kb_s ^ 1)
+      const int e0 = j * kMqTile + 32 * kb_s;
+      float mt = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = e0 + 8 * (e >> 2) + 4 * h2 + (e & 3);
+        const float v = key < nv ? s[e] * a.c2 : -INFINITY;
+        s[e] = v;
+        mt = fmaxf(mt, v);
+      }
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+        mt = fmaxf(mt, __uint_as_float(h2 ? sw[0] : sw[1]));
+      }
+      if (h2 == 0) pmax[kb_s * 64 + hl] = mt;
+      wait_lgkmcnt0();
+      lds_barrier();                    // both halves' maxima are in
+      mt = fmaxf(mt, pmax[(kb_s ^ 1) * 64 + hl]);
+      bool restart = false;
+      if (j == 0) m_ref = fmaxf(fmaxf(m_floor, s_sink), mt);
+      else restart = mt > m_ref + kMqHeadroom;
+      float psum = 0.f;
+      char* const prow = P + hl * 128;
+      const int pswz = (hl >> 1) & 7;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[i] = exp2_hw(s[4 * g + i] - m_ref);
+          psum += p[i];
         }
-        const uint2 lo = __builtin_bit_cast(uint2, part[0]), hi = __builtin_bit_cast(uint2, part[1]);
-        af[cb] = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        *reinterpret_cast<uint2*>(prow + (((4 * kb_s + g) ^ pswz) << 4) + 8 * h2) =
+            make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
       }
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        const int hd = 32 * hb + (lane & 31);
-        bfp[hb] = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const uint4*>(P + hd * 128 + (((2 * ks + h2) ^ ((hd >> 1) & 7)) << 4)));
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(psum), __float_as_uint(psum), false, false);
+        psum = h2 ? __uint_as_float(sw[0]) + psum : psum + __uint_as_float(sw[1]);
       }
+      if (h2 == 0) psm[kb_s * 64 + hl] = psum;
+      const bool any_restart = __ballot(restart) != 0;   // every lane votes, then lane 0 records it
+      if (lane == 0) flags[w] = any_restart ? 1 : 0;
+      wait_lgkmcnt0();
+      lds_barrier();                    // P, sums and votes of every head are in
+      l_run += psm[hl] + psm[64 + hl];
+      const bool restart_all = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint32_t*>(flags)) != 0;
+
+      // ---- values: O^T[col][head] += E^T[col][entry] P^T[entry][head]
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
+      for (int ks = 0; ks < 4; ++ks) {                  // 16 entries per step
+        bf16x8_t af[4], bfp[2];
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          typedef short v4s __attribute__((ext_vector_type(4)));
+          v4s part[2];
+#pragma unroll
+          for (int half = 0; half < 2; ++half)
+            part[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4s*)(E + troff[half][cb] + 16 * kMqRowBytes * ks));
+          const uint2 lo = __builtin_bit_cast(uint2, part[0]), hi = __builtin_bit_cast(uint2, part[1]);
+          af[cb] = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        }
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)
-          o[cb][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cb], bfp[hb], o[cb][hb], 0, 0, 0);
+          bfp[hb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(P + poff[ks] + 32 * 128 * hb));
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb)
+            o[cb][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cb], bfp[hb], o[cb][hb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);   // one step's fragments live at a time
+      }
+      // A restart ends the pass here, at the end of the tile, so that the loop
+      // body stays one block (the tile's own, overscaled, products are dropped
+      // with the rest of the pass).
+      if (restart_all) {
+        m_floor = fmaxf(m_ref, mt);     // at least this tile's maximum from now on
+        again = true;
+        break;
+      }
     }
+    if (!again) break;
+    wait_vmcnt<0>();                  // the copy of the tile after the restarting one has landed
+    lds_barrier();                    // and no wave reads a tile any more
   }
 
   wait_vmcnt<0>();                    // no copy into this workgroup's LDS outlives it
-  // ---- normalise and store: o[t][head][col] = O^T[col][head] / sum
+  // ---- normalise and store: o[t][head][col] = (O^T[col][head] + sink
+  // weight * v_sink[col]) / sum, the sum including the sink's weight
   if (kb_s == 0 && h2 == 0) {
-    inv[hl] = l_run > 0.f ? 1.f / l_run : 0.f;
-    if (a.lse)
-      a.lse[t * kMqaHeads + head0 + hl] =
-          l_run > 0.f ? (m_used + __log2f(l_run)) * 0.6931471805599453f : -INFINITY;
+    if (n_tiles == 0) m_ref = s_sink;                  // nothing visible: the sink alone (if any)
+    const float ws = a.k_sink ? exp2_hw(s_sink - m_ref) : 0.f;
+    const float l = l_run + ws;
+    inv[hl] = l > 0.f ? 1.f / l : 0.f;
+    sinkw[hl] = l > 0.f && a.v_sink ? ws / l : 0.f;
+    if (a.lse) a.lse[t * kMqaHeads + head0 + hl] = l > 0.f ? (m_ref + __log2f(l)) * 0.6931471805599453f : -INFINITY;
   }
   wait_lgkmcnt0();
   lds_barrier();
+  const uint16_t* const vs = reinterpret_cast<const uint16_t*>(a.v_sink);
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
     const int hd = 32 * hb + (lane & 31);
-    const float f = inv[hd];
+    const float f = inv[hd], fs = sinkw[hd];
     char* orow = a.out + (t * kMqaHeads + head0 + hd) * (int64_t)kMqaDim * (DOUT == DT_BF16 ? 2 : 4);
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int col = 128 * w + 32 * cb + 8 * g + 4 * h2;
-        const float v0 = o[cb][hb][4 * g] * f, v1 = o[cb][hb][4 * g + 1] * f;
-        const float v2 = o[cb][hb][4 * g + 2] * f, v3 = o[cb][hb][4 * g + 3] * f;
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = o[cb][hb][4 * g + i] * f;
+        if (vs) {
+          const uint2 sv = *reinterpret_cast<const uint2*>(vs + col);
+          v[0] = fmaf(fs, __uint_as_float(sv.x << 16), v[0]);
+          v[1] = fmaf(fs, __uint_as_float(sv.x & 0xffff0000u), v[1]);
+          v[2] = fmaf(fs, __uint_as_float(sv.y << 16), v[2]);
+          v[3] = fmaf(fs, __uint_as_float(sv.y & 0xffff0000u), v[3]);
+        }
         if (DOUT == DT_BF16)
-          *reinterpret_cast<uint2*>(orow + col * 2) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+          *reinterpret_cast<uint2*>(orow + col * 2) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
         else
-          *reinterpret_cast<float4*>(orow + col * 4) = make_float4(v0, v1, v2, v3);
+          *reinterpret_cast<float4*>(orow + col * 4) = make_float4(v[0], v[1], v[2], v[3]);
       }
   }
 }

@@ -57,15 +57,32 @@ def test_mqa_ragged_batch(gpu_device, sink, out_dtype):
     check_mqa(to64(out), O, A, out_dtype, to64(lse), L)
 
 
-def test_mqa_peaked_logits_rescale(gpu_device):
-    """Queries with std 4 make the attention peaked (logit std 4): the running
-    maximum of a head grows past the 8 (log2) headroom over the tiles, which
-    exercises the accumulator rescaling; 2000 entries, sink with value."""
+def test_mqa_peaked_logits(gpu_device):
+    """Queries with std 4 make the attention peaked (logit std 4): a few
+    entries carry most of the weight and the probabilities span a wide range
+    below the first tile's maximum; 2000 entries, sink with value."""
     case = synth.mqa_case([6], [2000], seed=2, device=gpu_device, q_std=4.0)
     nv = np.array([2000, 1999, 1000, 64, 63, 1500], dtype=np.int32)
     out, lse = _run(case, nv, "key+value", "f32")
     O, L, A = _ref(case, nv, np.arange(6), "key+value")
     check_mqa(to64(out), O, A, "f32", to64(lse), L)
+
+
+def test_mqa_growing_logits_restart(gpu_device):
+    """Logits that grow along the sequence far past the first tile's maximum:
+    entry s has s in dimension 0 and half the heads have 8 there, so their
+    logit rises by about 0.5 (log2 units) per entry -- over 64 above the
+    first tile's maximum by the third tile, and again later, which restarts
+    the sweep with a raised reference (several times for the longest
+    queries).  The other heads stay ordinary; sink with value."""
+    case = synth.mqa_case([4], [400], seed=3, device=gpu_device)
+    case.kv[:, 0] = torch.arange(400, device=gpu_device, dtype=torch.float32).to(torch.bfloat16)
+    case.q[:, :64, 0] = 8.0
+    nv = np.array([400, 333, 190, 129], dtype=np.int32)
+    for out_dtype in ("f32", "bf16"):
+        out, lse = _run(case, nv, "key+value", out_dtype)
+        O, L, A = _ref(case, nv, np.arange(4), "key+value")
+        check_mqa(to64(out), O, A, out_dtype, to64(lse), L)
 
 
 def test_mqa_full_config_sampled(gpu_device):
