@@ -39,6 +39,14 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
 }
 
+// s_waitcnt lgkmcnt(N) with vmcnt and expcnt left open: at most N LDS (or
+// scalar-memory) operations still outstanding.
+template <int N>
+__device__ __forceinline__ void wait_lgkmcnt() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (N << 8) | (3 << 14));
+}
+
 // s_waitcnt lgkmcnt(0) with vmcnt and expcnt left open.
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
 

@@ -41,6 +41,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
+// The same packing through gfx950's conversion instruction
+// (v_cvt_pk_bf16_f32, round to nearest even): one instruction for two values.
+// Equal to pack_bf16x2 on finite inputs.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // Four OCP E4M3FN codes packed little-endian in a word: v_cvt_pk_fp8_f32
 // rounds to nearest even into the OCP E4M3FN grid on gfx950 (a sweep of every
 // fp32 magnitude below 512, both signs, gave the same codes as f32_to_e4m3

@@ -16,22 +16,25 @@
 //  * scores: wave w forms the 32 x 32 block S^T = E Q^T of head block w & 1
 //    and entry block w >> 1 (A = entry fragments from LDS, B = the head
 //    block's query fragments, held in registers for the whole sweep).  Lane l
-//    then holds head l % 32 of the block and 16 of the 32 entries; one
-//    exchange between lanes l and l ^ 32 and one between the two waves that
-//    share a head block (through LDS) give the tile maximum per head.  The
-//    probabilities go to LDS as bf16, P[head][entry];
+//    then holds head l % 32 of the block and 16 of the 32 entries; an
+//    exchange between lanes l and l ^ 32 gives the wave's maximum per head.
+//    The probabilities go to LDS as bf16, P[head][entry];
 //  * values: wave w accumulates O^T = E^T P^T for output columns
 //    128 w .. 128 w + 127 of the 64 heads (8 accumulators of 32 x 32).  The
 //    A operand needs 8 consecutive entries of one column per lane: the gfx950
 //    transposing LDS read (ds_read_b64_tr_b16) delivers them from the
 //    row-major entry tile, 4 entries per read.
 // The softmax of a head is taken against a fixed reference: the larger of the
-// sink's logit and the first tile's maximum.  Later tiles may exceed it by up
-// to 64 (log2 units), so the accumulators are never rescaled; a tile that
-// exceeds it by more raises the reference and starts the sweep again (each
-// such restart moves past the tile that caused it, so there are at most as
-// many as tiles).  The sink joins the first tile's value phase as one more
-// entry, of key k_sink and value v_sink (or zero).
+// sink's logit and the first tile's maximum (over both waves of the head
+// block, exchanged through LDS).  Later tiles may exceed it by up to 64 (log2
+// units), so the accumulators are never rescaled and no later tile needs the
+// other wave's maximum; a tile that exceeds it by more raises the reference
+// and starts the sweep again (each such restart moves past the tile that
+// caused it, so there are at most as many as tiles).  Each wave sums the
+// probabilities of its own entries; the sums meet once, at the end, where the
+// sink's weight joins the sum and its weight times v_sink the output.  A tile
+// costs two workgroup barriers: its copy landed, and its probabilities
+// written.
 //
 // LDS: entry tiles 2 x 64 KiB; 16-byte chunk c of entry row r at slot
 // c ^ f(r), f(r) = ((r & 3) << 2) | ((r >> 2) & 3): the score phase's reads
@@ -143,7 +146,7 @@ __global__ __launch_bounds__(kMqThreads, 1) void mqa_sink_kernel(MqArgs a) {
 
   char* const P = lds + kMqPOff;
   float* const pmax = reinterpret_cast<float*>(lds + kMqMaxOff);   // [kb][64]
-  float* const psm = reinterpret_cast<float*>(lds + kMqSumOff);    // [kb][64]
+  float* const psm = reinterpret_cast<float*>(lds + kMqSumOff);    // [kb][64] sums at the end
   float* const sinkw = reinterpret_cast<float*>(lds + kMqFacOff);  // [64] sink weight / sum at the end
   float* const inv = reinterpret_cast<float*>(lds + kMqInvOff);    // [64]
   uint8_t* const flags = reinterpret_cast<uint8_t*>(lds + kMqFlagOff);
@@ -213,38 +216,68 @@ __global__ __launch_bounds__(kMqThreads, 1) void mqa_sink_kernel(MqArgs a) {
       asm volatile("" : "+v"(lane_v));
 
       // ---- scores S^T[entry][head]: entries 32 kb_s .., heads 32 hb_s ..
-      f32x16_t s = f32x16_t{};
+      // The entry fragments are read kSPre k-steps ahead of their MFMA; two
+      // accumulators (even and odd k-steps) keep consecutive MFMAs independent.
+      constexpr int kSPre = 4;
+      f32x4_t ef[kSPre];
+      const auto load_s = [&](int kk) { return *reinterpret_cast<const f32x4_t*>(E + koff[kk & 7] + 256 * (kk >> 3)); };
+#pragma unroll
+      for (int kk = 0; kk < kSPre; ++kk) ef[kk] = load_s(kk);
+      f32x16_t s2[2] = {f32x16_t{}, f32x16_t{}};
 #pragma unroll
       for (int kk = 0; kk < 32; ++kk) {
-        const f32x4_t ef = *reinterpret_cast<const f32x4_t*>(E + koff[kk & 7] + 256 * (kk >> 3));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ef), qf[kk], s, 0, 0, 0);
+        s2[kk & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ef[kk % kSPre]), qf[kk],
+                                                             s2[kk & 1], 0, 0, 0);
+        if (kk + kSPre < 32) ef[kk % kSPre] = load_s(kk + kSPre);
         // tile j + 1 (past the last tile: beyond the visible entries, where
         // the descriptor's range returns zeros or the rows are never read)
         if (kk & 1) issue_row(j + 1, kk >> 1, lane_v);
+        __builtin_amdgcn_sched_barrier(0);   // keep this order: the scheduler would sink the reads
       }
+      f32x16_t s = s2[0] + s2[1];
 
-      // ---- softmax of head hl over the tile (log2 units); the other 32
-      // entries of the tile are the partner wave's (kb_s ^ 1)
-      const int e0 = j * kMqTile + 32 * kb_s;
-      float mt = -INFINITY;
+      // ---- softmax of head hl over the wave's 32 entries of the tile (log2
+      // units); the other 32 are the partner wave's (kb_s ^ 1).  Only the
+      // first tile needs the maximum over both halves (it sets the
+      // reference); later tiles only test the headroom, which either half can
+      // do alone, and each wave sums its own half.
+      // A tile wholly inside the visible entries keeps the raw dot products
+      // (the logit is folded into the exponent's fused multiply-add below, and
+      // the maximum logit is the larger of scale * max and scale * min, for
+      // either sign of the scale); the tile that crosses the visible count
+      // turns them into logits, -inf where hidden, and scales by 1 below.
+      float mt, cs;
+      if ((j + 1) * kMqTile <= nv) {
+        float hi = s[0], lo = s[0];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = e0 + 8 * (e >> 2) + 4 * h2 + (e & 3);
-        const float v = key < nv ? s[e] * a.c2 : -INFINITY;
-        s[e] = v;
-        mt = fmaxf(mt, v);
+        for (int e = 1; e < 16; ++e) {
+          hi = fmaxf(hi, s[e]);
+          lo = fminf(lo, s[e]);
+        }
+        mt = fmaxf(hi * a.c2, lo * a.c2);
+        cs = a.c2;
+      } else {
+        const int e0 = j * kMqTile + 32 * kb_s;
+        mt = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = e0 + 8 * (e >> 2) + 4 * h2 + (e & 3);
+          s[e] = key < nv ? s[e] * a.c2 : -INFINITY;
+          mt = fmaxf(mt, s[e]);
+        }
+        cs = 1.f;
       }
       {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
         mt = fmaxf(mt, __uint_as_float(h2 ? sw[0] : sw[1]));
       }
-      if (h2 == 0) pmax[kb_s * 64 + hl] = mt;
-      wait_lgkmcnt0();
-      lds_barrier();                    // both halves' maxima are in
-      mt = fmaxf(mt, pmax[(kb_s ^ 1) * 64 + hl]);
-      bool restart = false;
-      if (j == 0) m_ref = fmaxf(fmaxf(m_floor, s_sink), mt);
-      else restart = mt > m_ref + kMqHeadroom;
+      if (j == 0) {
+        if (h2 == 0) pmax[kb_s * 64 + hl] = mt;
+        wait_lgkmcnt0();
+        lds_barrier();                  // both halves' maxima are in
+        m_ref = fmaxf(fmaxf(m_floor, s_sink), fmaxf(mt, pmax[(kb_s ^ 1) * 64 + hl]));
+      }
+      const bool restart = mt > m_ref + kMqHeadroom;   // never at the first tile
       float psum = 0.f;
       char* const prow = P + hl * 128;
       const int pswz = (hl >> 1) & 7;
@@ -253,54 +286,72 @@ __global__ __launch_bounds__(kMqThreads, 1) void mqa_sink_kernel(MqArgs a) {
         float p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[i] = exp2_hw(s[4 * g + i] - m_ref);
+          p[i] = exp2_hw(fmaf(s[4 * g + i], cs, -m_ref));
           psum += p[i];
         }
         *reinterpret_cast<uint2*>(prow + (((4 * kb_s + g) ^ pswz) << 4) + 8 * h2) =
-            make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+            make_uint2(cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3]));
       }
       {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(psum), __float_as_uint(psum), false, false);
-        psum = h2 ? __uint_as_float(sw[0]) + psum : psum + __uint_as_float(sw[1]);
+        l_run += h2 ? __uint_as_float(sw[0]) + psum : psum + __uint_as_float(sw[1]);
       }
-      if (h2 == 0) psm[kb_s * 64 + hl] = psum;
       const bool any_restart = __ballot(restart) != 0;   // every lane votes, then lane 0 records it
       if (lane == 0) flags[w] = any_restart ? 1 : 0;
-      wait_lgkmcnt0();
-      lds_barrier();                    // P, sums and votes of every head are in
-      l_run += psm[hl] + psm[64 + hl];
-      const bool restart_all = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint32_t*>(flags)) != 0;
 
-      // ---- values: O^T[col][head] += E^T[col][entry] P^T[entry][head]
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {                  // 16 entries per step
-        bf16x8_t af[4], bfp[2];
+      // ---- values: O^T[col][head] += E^T[col][entry] P^T[entry][head], 16
+      // entries per step, the next step's fragments read during this one's
+      // MFMAs.  The first step's entry fragments are read before the barrier
+      // (the tile has been in place since the top of the tile); the wait
+      // below leaves exactly those 8 reads open, so this wave's P and vote
+      // writes are complete when it reaches the barrier.
+      bf16x8_t af[2][4], bp[2][2];
+      const auto load_e = [&](int ks, bf16x8_t (&f)[4]) {
+        typedef short v4s __attribute__((ext_vector_type(4)));
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
-          typedef short v4s __attribute__((ext_vector_type(4)));
           v4s part[2];
 #pragma unroll
           for (int half = 0; half < 2; ++half)
             part[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (__attribute__((address_space(3))) v4s*)(E + troff[half][cb] + 16 * kMqRowBytes * ks));
           const uint2 lo = __builtin_bit_cast(uint2, part[0]), hi = __builtin_bit_cast(uint2, part[1]);
-          af[cb] = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+          f[cb] = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
         }
+      };
+      const auto load_p = [&](int ks, bf16x8_t (&f)[2]) {
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)
-          bfp[hb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(P + poff[ks] + 32 * 128 * hb));
+          f[hb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(P + poff[ks] + 32 * 128 * hb));
+      };
+      asm volatile("" ::: "memory");   // the P and vote writes are issued before the reads below
+      load_e(0, af[0]);
+      wait_lgkmcnt<8>();
+      lds_barrier();                    // P and votes of every head are in
+      const bool restart_all = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint32_t*>(flags)) != 0;
+      load_p(0, bp[0]);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        if (ks < 3) {
+          load_e(ks + 1, af[(ks + 1) & 1]);
+          load_p(ks + 1, bp[(ks + 1) & 1]);
+        }
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
           for (int hb = 0; hb < 2; ++hb)
-            o[cb][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cb], bfp[hb], o[cb][hb], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);   // one step's fragments live at a time
+            o[cb][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][cb], bp[ks & 1][hb], o[cb][hb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);   // two steps' fragments live at a time
       }
       // A restart ends the pass here, at the end of the tile, so that the loop
       // body stays one block (the tile's own, overscaled, products are dropped
       // with the rest of the pass).
       if (restart_all) {
-        m_floor = fmaxf(m_ref, mt);     // at least this tile's maximum from now on
+        if (h2 == 0) pmax[kb_s * 64 + hl] = mt;
+        wait_lgkmcnt0();
+        lds_barrier();                  // both halves' maxima are in
+        // at least this tile's maximum from now on
+        m_floor = fmaxf(m_ref, fmaxf(mt, pmax[(kb_s ^ 1) * 64 + hl]));
         again = true;
         break;
       }
@@ -313,10 +364,13 @@ __global__ __launch_bounds__(kMqThreads, 1) void mqa_sink_kernel(MqArgs a) {
   wait_vmcnt<0>();                    // no copy into this workgroup's LDS outlives it
   // ---- normalise and store: o[t][head][col] = (O^T[col][head] + sink
   // weight * v_sink[col]) / sum, the sum including the sink's weight
+  if (h2 == 0) psm[kb_s * 64 + hl] = l_run;           // each wave's sum covers its entry half
+  wait_lgkmcnt0();
+  lds_barrier();
   if (kb_s == 0 && h2 == 0) {
     if (n_tiles == 0) m_ref = s_sink;                  // nothing visible: the sink alone (if any)
     const float ws = a.k_sink ? exp2_hw(s_sink - m_ref) : 0.f;
-    const float l = l_run + ws;
+    const float l = psm[hl] + psm[64 + hl] + ws;
     inv[hl] = l > 0.f ? 1.f / l : 0.f;
     sinkw[hl] = l > 0.f && a.v_sink ? ws / l : 0.f;
     if (a.lse) a.lse[t * kMqaHeads + head0 + hl] = l > 0.f ? (m_ref + __log2f(l)) * 0.6931471805599453f : -INFINITY;
