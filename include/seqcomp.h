@@ -183,8 +183,12 @@ int seqcomp_compress_fused(int mode, int64_t m, const void* H, int64_t d, int in
  *             the sequence's next append.  May be the same pointer as
  *             state_in (updated in place); must not overlap it otherwise.
  *   out       [nb x c] of out_dtype; out_scale [nb] fp32 for fp8 output.
- *   workspace seqcomp_append_workspace_bytes(nb, c, out_dtype) bytes (0
- *             unless the output is fp8).
+ *   workspace seqcomp_append_workspace_bytes(nb, c, out_dtype) bytes: for
+ *             batches of fewer than 129 tiles of 256 rows x 64 channels, the
+ *             fp32 partial products of a K loop split over up to 16
+ *             workgroups per tile (256 KiB per workgroup: 32 MiB at nb = 64,
+ *             c = 512); for an fp8 output, nb x c fp32 of staging.  0 when
+ *             neither applies.
  *   Requires d % 64 == 0, c % 16 == 0.  nb == 0 returns SEQCOMP_OK.
  * Appending a sequence's blocks one call at a time gives the same entries as
  * seqcomp_compress_fused over the whole sequence (up to rounding order).

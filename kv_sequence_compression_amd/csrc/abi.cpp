@@ -340,10 +340,15 @@ int seqcomp_compress_fused(int mode, int64_t m, const void* H, int64_t d, int in
   return hip_status(e);
 }
 
+// Split-K partial products (small batches), then the fp32 staging of an fp8 output.
+static size_t append_partial_region(int64_t nb, int64_t c) { return round_up(append_partial_bytes(nb, (int)c), 256); }
+
 size_t seqcomp_append_workspace_bytes(int64_t nb, int64_t c, int out_dtype) {
-  if (nb < 0 || c < 1 || !valid_out_dtype(out_dtype)) return (size_t)-1;
-  if (nb == 0 || out_dtype != SEQCOMP_FP8_E4M3) return 0;
-  return round_up((size_t)nb * c * 4, 256);
+  if (nb < 0 || nb * 4 > kMaxRows || c < 1 || c > (int64_t(1) << 20) || !valid_out_dtype(out_dtype))
+    return (size_t)-1;
+  if (nb == 0) return 0;
+  const size_t staging = out_dtype == SEQCOMP_FP8_E4M3 ? round_up((size_t)nb * c * 4, 256) : 0;
+  return append_partial_region(nb, c) + staging;
 }
 
 int seqcomp_csa_append(const void* H, int64_t nb, int64_t d, int in_dtype, const void* Wt, int64_t c,
@@ -383,9 +388,12 @@ int seqcomp_csa_append(const void* H, int64_t nb, int64_t d, int in_dtype, const
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool fp8 = out_dtype == SEQCOMP_FP8_E4M3;
-  void* dst = fp8 ? workspace : out;
+  const size_t part_bytes = append_partial_region(nb, c);
+  void* partial = part_bytes ? workspace : nullptr;
+  void* dst = fp8 ? static_cast<char*>(workspace) + part_bytes : out;
   const int dst_dt = fp8 ? DT_F32 : out_dtype;
-  hipError_t e = launch_csa_append(in_dtype, dst_dt, H, nb, (int)d, Wt, (int)c, Ba, Bb, state_in, state_out, dst, s);
+  hipError_t e =
+      launch_csa_append(in_dtype, dst_dt, H, nb, (int)d, Wt, (int)c, Ba, Bb, state_in, state_out, dst, partial, s);
   if (e == hipSuccess && fp8)
     e = launch_quant_fp8(reinterpret_cast<const float*>(dst), nb, (int)c, static_cast<uint8_t*>(out), out_scale, s);
   return hip_status(e);

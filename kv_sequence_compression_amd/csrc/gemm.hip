@@ -555,6 +555,21 @@ __device__ void epilogue_csa(const Args& a, WaveAcc& acc, const TileRec& t, int 
 // rule of eq. attn-seqcomp-overlap-bound); the block's own b-partial becomes
 // the state for its successor.  Same accumulator layout as epilogue_csa: run
 // q of lane half h is block 32 wm + 8 ms + 2 q + h of the tile.
+// One append entry: block j's a-partial merged with its previous block's
+// b-partial gives the entry; block j's own b-partial becomes the new state.
+template <int DOUT>
+__device__ __forceinline__ void append_store(const Args& a, const SoftAcc& pa, const SoftAcc& pb, const SoftAcc& prev,
+                                             int64_t j, bool ok, int ch) {
+  const SoftAcc m = softacc_merge(pa, prev);
+  if (ok && j < a.nb) {
+    store1<DOUT>(a.out, j * a.c + ch, m.A / m.S);
+    float* so = a.state_out + j * 3 * a.c + ch;
+    so[0] = pb.M;
+    so[a.c] = pb.S;
+    so[2 * a.c] = pb.A;
+  }
+}
+
 template <int DOUT>
 __device__ void epilogue_csa_append(const Args& a, WaveAcc& acc, int mt, int nt, int lane, int wm, int wn,
                                     const float (&ba)[4], const float (&bb)[4]) {
@@ -579,15 +594,7 @@ __device__ void epilogue_csa_append(const Args& a, WaveAcc& acc, int mt, int nt,
     for (int q = 0; q < 4; ++q) {
       const SoftAcc pa = partial4(acc[ms][2], acc[ms][0], q, ba);
       const SoftAcc pb = partial4(acc[ms][3], acc[ms][1], q, bb);
-      const int64_t j = j0 + wm * 32 + ms * 8 + q * 2 + h;
-      const SoftAcc m = softacc_merge(pa, prev[ms * 4 + q]);
-      if (ok && j < a.nb) {
-        store1<DOUT>(a.out, j * c + ch, m.A / m.S);
-        float* so = a.state_out + j * 3 * c + ch;
-        so[0] = pb.M;
-        so[c] = pb.S;
-        so[2 * c] = pb.A;
-      }
+      append_store<DOUT>(a, pa, pb, prev[ms * 4 + q], j0 + wm * 32 + ms * 8 + q * 2 + h, ok, ch);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -729,6 +736,130 @@ __global__ __launch_bounds__(256) void csa_fixup_kernel(const TileRec* __restric
   }
 }
 
+// Split-K form of the CSA append, for batches too small to fill the chip with
+// 256 x 256 tiles (64 blocks are one row of 8 tiles, each of which would walk
+// all of K on one CU).  Workgroup (L, s) multiplies K slabs
+// [s nk / S, (s + 1) nk / S) of logical tile L and stores its accumulators as
+// they sit in registers; append_reduce_kernel adds the S partials of one
+// wave's 32-row M subtile and runs the append epilogue on the sum.  Partial
+// layout, in float4: [L][s][wave][ms][N subtile][element quad][lane], so
+// every store and load is one coalesced 1 KiB row.
+constexpr int kAppendMaxSplits = 16;
+constexpr int kAppendSplitTarget = 256;        // workgroups to aim for: one per CU of an MI355X
+constexpr int kPartialQuads = 4 * 4 * 64;      // float4 per (L, s, wave, ms) block: 16 KiB
+
+__device__ __forceinline__ int64_t partial_base(int64_t L, int S, int s, int w, int ms) {
+  return (((L * S + s) * 4 + w) * 4 + ms) * kPartialQuads;
+}
+
+template <int DIN>
+__global__ __launch_bounds__(kThreads, 1) void append_splitk_kernel(Args a, int S, float4* __restrict__ partial) {
+  __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
+  const int L = blockIdx.x / S, sp = blockIdx.x - L * S;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int mt = L / a.n_nt, nt = L - mt * a.n_nt;
+  const int wm = w >> 1, wn = w & 1;
+  const int64_t row0 = (int64_t)mt * kTile;
+  const int nvalid = (int)min<int64_t>(kTile, a.T - row0);
+  const int k0 = (int)((int64_t)sp * a.nk / S), k1 = (int)((int64_t)(sp + 1) * a.nk / S);   // S <= nk: k1 > k0
+  uint32_t a_off[kLoadsPerSlab], b_off[kLoadsPerSlab];
+#pragma unroll
+  for (int i = 0; i < kLoadsPerSlab; ++i) {
+    const int r = w * 64 + i * 8 + (lane >> 3);
+    const int kc = (lane & 7) ^ swz_f(r);
+    a_off[i] = (uint32_t)(min(r, nvalid - 1) * a.lda + kc * 16);
+    b_off[i] = (uint32_t)((int64_t)b_row_of<MODE_CSA_APPEND>(r, nt, a.c, a.n_out) * a.lda + kc * 16);
+  }
+  WaveAcc acc;
+  mainloop<DIN>(a.H + row0 * a.lda + (int64_t)k0 * kRowBytes, a_off, a.Wt + (int64_t)k0 * kRowBytes, b_off, k1 - k0,
+                lds, w, lane, wm, wn, acc);
+#pragma unroll
+  for (int ms = 0; ms < 4; ++ms) {
+    float4* dst = partial + partial_base(L, S, sp, w, ms) + lane;
+#pragma unroll
+    for (int jn = 0; jn < 4; ++jn)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        // each element through a VGPR: a store fed straight from an
+        // accumulator register has been miscompiled (see epilogue_project)
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = acc[ms][jn][4 * q4 + e];
+          asm volatile("" : "+v"(v[e]));
+        }
+        dst[(jn * 4 + q4) * 64] = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Workgroup = one wave: (tile L, wave w, M subtile ms).  Four splits' loads
+// are in flight at a time; the sum runs in split order, so it is the same on
+// every call.
+template <int DOUT>
+__global__ __launch_bounds__(64) void append_reduce_kernel(Args a, int S, const float4* __restrict__ partial) {
+  const int L = blockIdx.x >> 4, w = (blockIdx.x >> 2) & 3, ms = blockIdx.x & 3;
+  const int lane = threadIdx.x;
+  const int mt = L / a.n_nt, nt = L - mt * a.n_nt;
+  const int wm = w >> 1, wn = w & 1;
+  f32x16_t acc[4];
+#pragma unroll
+  for (int jn = 0; jn < 4; ++jn) acc[jn] = f32x16_t{};
+  for (int s0 = 0; s0 < S; s0 += 4) {
+    float4 v[4][16];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float4* src = partial + partial_base(L, S, min(s0 + u, S - 1), w, ms) + lane;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) v[u][k] = src[k * 64];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (s0 + u < S) {
+#pragma unroll
+        for (int jn = 0; jn < 4; ++jn)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            acc[jn][4 * q4 + 0] += v[u][jn * 4 + q4].x;
+            acc[jn][4 * q4 + 1] += v[u][jn * 4 + q4].y;
+            acc[jn][4 * q4 + 2] += v[u][jn * 4 + q4].z;
+            acc[jn][4 * q4 + 3] += v[u][jn * 4 + q4].w;
+          }
+      }
+    }
+  }
+  float ba[4], bb[4];
+  csa_bias(a, nt, lane, wn, ba, bb);
+  const int col = lane & 31, h = lane >> 5;
+  const int ch = nt * 64 + wn * 32 + col;
+  const bool ok = ch < a.c;
+  const int64_t j0 = (int64_t)mt * 64 + wm * 32 + ms * 8 + h;
+  SoftAcc prev[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t j = min(j0 + q * 2, a.nb - 1);
+    const float* st = a.state_in + j * 3 * a.c + min(ch, a.c - 1);
+    prev[q] = SoftAcc{st[0], st[a.c], st[2 * a.c]};
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const SoftAcc pa = partial4(acc[2], acc[0], q, ba);
+    const SoftAcc pb = partial4(acc[3], acc[1], q, bb);
+    append_store<DOUT>(a, pa, pb, prev[q], j0 + q * 2, ok, ch);
+  }
+}
+
+// Splits of the append's K loop for a batch of nb blocks and c channels (1:
+// no split).
+int append_splits(int64_t nb, int c) {
+  const int64_t G = ((4 * nb + kTile - 1) / kTile) * ((c + 63) / 64);
+  if (G <= 0 || G * 2 > kAppendSplitTarget) return 1;
+  const int64_t S = kAppendSplitTarget / G;
+  return S < kAppendMaxSplits ? (int)S : kAppendMaxSplits;
+}
+
 // Compute units of the current device (one workgroup of the tile kernels fits per CU).
 int cu_count() {
   static int cached[64] = {0};
@@ -804,9 +935,16 @@ hipError_t launch_fused(int mode, int in_dt, int out_dt, const void* H, int d, c
   return dispatch<MODE_HCA>(in_dt, out_dt, a, stream);
 }
 
+size_t append_partial_bytes(int64_t nb, int c) {
+  const int S = append_splits(nb, c);
+  if (S <= 1) return 0;
+  const int64_t G = ((4 * nb + kTile - 1) / kTile) * ((c + 63) / 64);
+  return (size_t)G * S * 4 * 4 * kPartialQuads * sizeof(float4);
+}
+
 hipError_t launch_csa_append(int in_dt, int out_dt, const void* H, int64_t nb, int d, const void* Wt, int c,
                              const float* Ba, const float* Bb, const float* state_in, float* state_out, void* out,
-                             hipStream_t stream) {
+                             void* partial, hipStream_t stream) {
   Args a{};
   const int es = in_dt == DT_BF16 ? 2 : 4;
   a.H = static_cast<const char*>(H);
@@ -824,7 +962,21 @@ hipError_t launch_csa_append(int in_dt, int out_dt, const void* H, int64_t nb, i
   a.n_out = 1;
   a.n_mt = (int)((a.T + kTile - 1) / kTile);
   a.n_nt = (c + 63) / 64;
-  return dispatch<MODE_CSA_APPEND>(in_dt, out_dt, a, stream);
+  const int S = min(append_splits(nb, c), a.nk);
+  if (S <= 1 || partial == nullptr) return dispatch<MODE_CSA_APPEND>(in_dt, out_dt, a, stream);
+  const int G = a.n_mt * a.n_nt;
+  float4* part = static_cast<float4*>(partial);
+  if (in_dt == DT_BF16)
+    hipLaunchKernelGGL(append_splitk_kernel<DT_BF16>, dim3(G * S), dim3(kThreads), 0, stream, a, S, part);
+  else
+    hipLaunchKernelGGL(append_splitk_kernel<DT_F32>, dim3(G * S), dim3(kThreads), 0, stream, a, S, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (out_dt == DT_BF16)
+    hipLaunchKernelGGL(append_reduce_kernel<DT_BF16>, dim3(G * 16), dim3(64), 0, stream, a, S, part);
+  else
+    hipLaunchKernelGGL(append_reduce_kernel<DT_F32>, dim3(G * 16), dim3(64), 0, stream, a, S, part);
+  return hipGetLastError();
 }
 
 hipError_t launch_csa_fixup(int out_dt, const TileRec* tiles, int n_tiles, int c, const float* halo, void* out,

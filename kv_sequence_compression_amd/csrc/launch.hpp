@@ -55,9 +55,14 @@ hipError_t launch_fused(int mode, int in_dt, int out_dt, const void* H, int d, c
 // CSA decode append: nb independent blocks of 4 rows of H; entry j merges
 // block j's a-partial with state_in[j] (the previous block's b-partial, fp32
 // [nb][3][c]) and block j's b-partial goes to state_out[j].
+// Batches that fill fewer than 129 tiles split the K loop over up to 16
+// workgroups per tile; `partial` (append_partial_bytes(nb, c) bytes, null
+// when that is 0) holds their fp32 products until a reduce kernel sums them
+// and runs the same epilogue.
 hipError_t launch_csa_append(int in_dt, int out_dt, const void* H, int64_t nb, int d, const void* Wt, int c,
                              const float* Ba, const float* Bb, const float* state_in, float* state_out, void* out,
-                             hipStream_t stream);
+                             void* partial, hipStream_t stream);
+size_t append_partial_bytes(int64_t nb, int c);
 
 // Partial RoPE + mixed store of packed entries [E x c] (tiles of 64 entries
 // from the planner with tile_rows = 64 m).

@@ -173,7 +173,7 @@ STATE, STATE2 = 0x90000000, 0x98000000
 
 def append(lib, **kw):
     a = dict(H=A, nb=100, d=7168, in_dt=_lib.BF16, Wt=B_, c=512, Ba=BIAS, Bb=BIAS2, st_in=STATE, st_out=STATE2,
-             out=OUT, out_dt=_lib.BF16, scale=0, ws=0, ws_bytes=0)
+             out=OUT, out_dt=_lib.BF16, scale=0, ws=WS, ws_bytes=1 << 27)
     a.update(kw)
     return lib.seqcomp_csa_append(a["H"], a["nb"], a["d"], a["in_dt"], a["Wt"], a["c"], a["Ba"], a["Bb"],
                                   a["st_in"], a["st_out"], a["out"], a["out_dt"], a["scale"], a["ws"], a["ws_bytes"],
@@ -182,8 +182,17 @@ def append(lib, **kw):
 
 def test_append_workspace(lib):
     f = lib.seqcomp_append_workspace_bytes
-    assert f(100, 512, _lib.BF16) == 0 and f(0, 512, _lib.FP8_E4M3) == 0
-    assert f(100, 512, _lib.FP8_E4M3) == 100 * 512 * 4
+    part = 256 * 1024                                    # split-K partials of one workgroup
+    # 64 blocks, c = 512: 1 x 8 tiles, K split 16 ways
+    assert f(64, 512, _lib.BF16) == 8 * 16 * part
+    # 100 blocks: 2 x 8 tiles, 16 ways; fp8 adds the fp32 staging of the entries
+    assert f(100, 512, _lib.BF16) == 16 * 16 * part
+    assert f(100, 512, _lib.FP8_E4M3) == 16 * 16 * part + 100 * 512 * 4
+    # 1024 blocks: 16 x 8 = 128 tiles, split 2 ways; 4096 blocks: 512 tiles, no split
+    assert f(1024, 512, _lib.BF16) == 128 * 2 * part
+    assert f(4096, 512, _lib.BF16) == 0
+    assert f(4096, 512, _lib.FP8_E4M3) == 4096 * 512 * 4
+    assert f(0, 512, _lib.FP8_E4M3) == 0
     assert f(-1, 512, _lib.BF16) == ctypes.c_size_t(-1).value
     assert f(1, 512, 9) == ctypes.c_size_t(-1).value
 
@@ -201,7 +210,8 @@ def test_append_workspace(lib):
     (dict(st_out=0), "SEQCOMP_E_NULL"),
     (dict(out=0), "SEQCOMP_E_NULL"),
     (dict(out_dt=_lib.FP8_E4M3, scale=0, ws=WS, ws_bytes=1 << 20), "SEQCOMP_E_NULL"),
-    (dict(out_dt=_lib.FP8_E4M3, scale=SCALE), "SEQCOMP_E_WORKSPACE"),
+    (dict(out_dt=_lib.FP8_E4M3, scale=SCALE, ws_bytes=16 * 16 * 256 * 1024), "SEQCOMP_E_WORKSPACE"),
+    (dict(ws=0, ws_bytes=0), "SEQCOMP_E_WORKSPACE"),     # the split-K partials of a small batch
     (dict(st_in=STATE + 4), "SEQCOMP_E_ALIGN"),
     (dict(st_out=STATE + 16), "SEQCOMP_E_ALIAS"),          # partial overlap with the input state
     (dict(st_out=A + 4096), "SEQCOMP_E_ALIAS"),            # the new state over H

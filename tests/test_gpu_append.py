@@ -85,6 +85,27 @@ def test_append_bf16_in_place_and_fp8(gpu_device):
     check_fp8(q, s, ref, 2e-2)
 
 
+def test_append_split_k_full_depth(gpu_device):
+    """64 sequences of two blocks at the full projection depth (d = 7168,
+    bf16, c = 512): one row of 8 tiles, so each call splits K over 16
+    workgroups per tile; both appends against the oracle."""
+    case = synth.compressor_case("csa", [8] * 64, 7168, 512, 4, seed=6, in_dtype="bf16", bias_std=0.3,
+                                 device=gpu_device)
+    ref = _oracle(case)
+    out, _ = _append_all(case, "bf16", in_place=True)
+    assert row_rel_err(to64(out), ref).max() <= 2e-2
+
+
+def test_append_unsplit_many_tiles(gpu_device):
+    """520 single-block sequences with c = 1024 make 9 x 16 = 144 tiles, more
+    than the split-K path takes: the K loop runs whole in each tile."""
+    case = synth.compressor_case("csa", [4] * 520, 64, 1024, 4, seed=7, in_dtype="f32", bias_std=0.3,
+                                 device=gpu_device)
+    ref = _oracle(case)
+    out, _ = _append_all(case, "f32", in_place=False)
+    assert max_abs_err(to64(out), ref) <= 2e-5
+
+
 def test_append_agrees_with_fused(gpu_device):
     """One append of every sequence's second block, fed the state of its first
     block, equals entry 1 of the fused compressor over the two blocks."""
