@@ -355,7 +355,10 @@ __global__ __launch_bounds__(kIxThreads, 1) void indexer_topk_kernel(IxArgs a) {
         cand_i[pos] = key;
       }
       cnt += __popcll(m);
-      wave_lds_sync();
+      // Compiler ordering only: LDS operations of one wave complete in
+      // order, and only this wave reads its buffer, so no wait is needed
+      // (one would also stall on the key fragments already in flight).
+      asm volatile("" ::: "memory");
     }
   };
 
