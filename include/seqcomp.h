@@ -291,9 +291,13 @@ size_t seqcomp_indexer_workspace_bytes(const int64_t* cu_q_host, int64_t batch);
  *   lse      [T x 128] fp32 or NULL: natural log of the softmax denominator
  *            of the scaled logits (sink included); -inf when nothing is
  *            visible and there is no sink (then out is zero).
- * Products are exact bf16 x bf16 in fp32; the probabilities are rounded to
- * bf16 for the value product.  Requires n_heads == 128, head_dim == 512,
- * bf16 q / kv / sink, and fewer than 2^21 entries per sequence.
+ * Products are exact bf16 x bf16 in fp32; the entries' probabilities are
+ * rounded to bf16 for the value product, the sink's weight times v_sink is
+ * added in fp32.  The softmax runs against a fixed per-head reference, so
+ * entry and sink values must stay below 2^43 in magnitude (fp32 sums of up
+ * to 2^21 terms of 2^64 times a value).  Requires n_heads == 128,
+ * head_dim == 512, bf16 q / kv / sink, and fewer than 2^21 entries per
+ * sequence.
  *   workspace: seqcomp_mqa_workspace_bytes(cu_q_host, batch) bytes.
  */
 int seqcomp_shared_kv_mqa(const void* q, const void* kv, int64_t n_heads, int64_t head_dim, int in_dtype,
