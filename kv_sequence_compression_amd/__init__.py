@@ -21,6 +21,7 @@ uint8 with one fp32 scale per entry).
 
 from __future__ import annotations
 
+import collections
 import ctypes
 
 import numpy as np
@@ -72,6 +73,37 @@ def _in_code(t: torch.Tensor) -> int:
     return _TORCH_IN[t.dtype]
 
 
+_DEV_COPIES = collections.OrderedDict()   # (device, stream, dtype, bytes) -> read-only device tensor
+_DEV_COPIES_MAX = 64
+_DEV_COPY_MAX_BYTES = 1 << 16
+
+
+def _to_device(a, dtype, device):
+    """`a` on `device` as a contiguous tensor of `dtype`, never written by the
+    library.  Small host arrays (sequence offsets, visible counts) are kept
+    by content, so a call that repeats a batch layout copies nothing; others
+    go through a freshly pinned buffer and an asynchronous copy on the
+    current stream.  A copy from pageable memory would make the host wait for
+    the stream to drain, leaving the GPU idle between back-to-back calls."""
+    if isinstance(a, torch.Tensor) and a.device.type != "cpu":
+        return a.to(device=device, dtype=dtype).contiguous()
+    t = torch.as_tensor(np.ascontiguousarray(np.asarray(a)), dtype=dtype).contiguous()
+    key = None
+    if t.numel() * t.element_size() <= _DEV_COPY_MAX_BYTES:
+        # the stream is part of the key: the copy was ordered on it
+        key = (str(torch.device(device)), torch.cuda.current_stream(device).cuda_stream, dtype, t.numpy().tobytes())
+        hit = _DEV_COPIES.get(key)
+        if hit is not None:
+            _DEV_COPIES.move_to_end(key)
+            return hit
+    d = t.pin_memory().to(device, non_blocking=True)
+    if key is not None:
+        _DEV_COPIES[key] = d
+        if len(_DEV_COPIES) > _DEV_COPIES_MAX:
+            _DEV_COPIES.popitem(last=False)
+    return d
+
+
 def _cu_arrays(cu_seqlens, device):
     """Host int64 array (kept alive by the caller) and its device copy."""
     if isinstance(cu_seqlens, torch.Tensor):
@@ -79,8 +111,7 @@ def _cu_arrays(cu_seqlens, device):
     else:
         host = np.asarray(cu_seqlens, dtype=np.int64)
     host = np.ascontiguousarray(host, dtype=np.int64)
-    dev = torch.from_numpy(host).to(device)
-    return host, dev
+    return host, _to_device(host, torch.int64, device)
 
 
 def _i64p(host: np.ndarray):
@@ -252,8 +283,8 @@ def rope_store(entries, m: int, cu_seqlens, cache, rope_dims: int = 64, rope_bas
     n_slots = scale.shape[0]
     if nope.shape != (n_slots, c - rope_dims) or rope.shape != (n_slots, rope_dims):
         raise ValueError("cache shapes do not match c and rope_dims")
-    p0 = None if pos0 is None else torch.as_tensor(pos0, dtype=torch.int64, device=dev).contiguous()
-    sl = None if slots is None else torch.as_tensor(slots, dtype=torch.int64, device=dev).contiguous()
+    p0 = None if pos0 is None else _to_device(pos0, torch.int64, dev)
+    sl = None if slots is None else _to_device(slots, torch.int64, dev)
     ws_n = lib().seqcomp_rope_store_workspace_bytes(int(m), _i64p(host), host.size - 1)
     ws = _alloc_ws(ws_n, dev)
     _check(lib().seqcomp_rope_store(_ptr(entries), _in_code(entries), c, int(m), _i64p(host), _ptr(cu_dev),
@@ -280,7 +311,7 @@ def indexer_topk(q, w, keys, k: int, cu_q=None, cu_k=None, n_valid=None, with_sc
     hk, ck = _cu_arrays([0, N] if cu_k is None else cu_k, dev)
     if hq.size != hk.size:
         raise ValueError("cu_q and cu_k must describe the same number of sequences")
-    nv = None if n_valid is None else torch.as_tensor(n_valid, dtype=torch.int32, device=dev).contiguous()
+    nv = None if n_valid is None else _to_device(n_valid, torch.int32, dev)
     idx = torch.empty((T, int(k)), dtype=torch.int32, device=dev)
     sc = torch.empty((T, int(k)), dtype=torch.float32, device=dev) if with_scores else None
     ws_n = lib().seqcomp_indexer_workspace_bytes(_i64p(hq), hq.size - 1)
@@ -312,7 +343,7 @@ def shared_kv_mqa(q, kv, cu_q=None, cu_k=None, n_valid=None, k_sink=None, v_sink
     hk, ck = _cu_arrays([0, N] if cu_k is None else cu_k, dev)
     if hq.size != hk.size:
         raise ValueError("cu_q and cu_k must describe the same number of sequences")
-    nv = None if n_valid is None else torch.as_tensor(n_valid, dtype=torch.int32, device=dev).contiguous()
+    nv = None if n_valid is None else _to_device(n_valid, torch.int32, dev)
     sc_ = float(scale) if scale is not None else 1.0 / float(np.sqrt(q.shape[2]))
     out = torch.empty(tuple(q.shape), dtype=_TORCH_OUT[out_dtype], device=dev)
     lse = torch.empty((T, q.shape[1]), dtype=torch.float32, device=dev) if with_lse else None

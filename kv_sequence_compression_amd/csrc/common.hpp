@@ -50,6 +50,45 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Cross-lane exchanges in registers, with no LDS round trip (__shfl_xor
+// compiles to ds_bpermute).  Lane index = threadIdx.x % 64 (blocks of whole
+// waves).  gfx950: DPP row_ror:8 within each row of 16 lanes;
+// v_permlane16_swap exchanges rows 0 <-> 1 and 2 <-> 3; v_permlane32_swap
+// the two halves.  Each swap returns the pair (first operand, second operand)
+// after the exchange: with both operands x, a lane of an even row (lower
+// half) finds its partner's value in the second, of an odd row (upper half)
+// in the first.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v);
+__device__ __forceinline__ float lane_xor8(float x) { return dpp_f32<0x128>(x); }   // row_ror:8
+__device__ __forceinline__ float lane_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float lane_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+// Maximum over the 64 lanes of a wave, in every lane: DPP quad swaps and
+// row mirrors give each row of 16 its maximum, the two swaps combine rows.
+// Every lane of the wave must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float wave_max_f32(float x) {
+  x = fmaxf(x, dpp_f32<0xB1>(x));      // quad_perm [1, 0, 3, 2]
+  x = fmaxf(x, dpp_f32<0x4E>(x));      // quad_perm [2, 3, 0, 1]
+  x = fmaxf(x, dpp_f32<0x141>(x));     // row_half_mirror
+  x = fmaxf(x, dpp_f32<0x140>(x));     // row_mirror
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Four OCP E4M3FN codes packed little-endian in a word: v_cvt_pk_fp8_f32
 // rounds to nearest even into the OCP E4M3FN grid on gfx950 (a sweep of every
 // fp32 magnitude below 512, both signs, gave the same codes as f32_to_e4m3

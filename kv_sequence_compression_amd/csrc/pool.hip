@@ -260,12 +260,14 @@ __global__ __launch_bounds__(kPoolThreads) void pool_hca_kernel(
       }
       fold_chunk<DIN, !FULL>(acc, z, x, bias, valid);
     }
+    // row groups g ^ 1, g ^ 2, g ^ 4 are lanes l ^ 8, l ^ 16, l ^ 32: exchanged
+    // in registers (DPP, lane swaps), not through LDS
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       SoftAcc s = acc[j];
-#pragma unroll
-      for (int mask = 8; mask <= 32; mask <<= 1)
-        s = softacc_merge(s, SoftAcc{__shfl_xor(s.M, mask, 64), __shfl_xor(s.S, mask, 64), __shfl_xor(s.A, mask, 64)});
+      s = softacc_merge(s, SoftAcc{lane_xor8(s.M), lane_xor8(s.S), lane_xor8(s.A)});
+      s = softacc_merge(s, SoftAcc{lane_xor16(s.M), lane_xor16(s.S), lane_xor16(s.A)});
+      s = softacc_merge(s, SoftAcc{lane_xor32(s.M), lane_xor32(s.S), lane_xor32(s.A)});
       acc[j] = s;
     }
     if (g == 0 && vok) store_entry8<DOUT>(acc, out + ((int64_t)(t.entry_start + e) * c + ch0 + v * 8) * OS);

@@ -16,12 +16,6 @@ namespace {
 
 constexpr int kQuantThreads = 256;
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
-  return x;
-}
-
 __global__ __launch_bounds__(kQuantThreads) void quant_fp8_kernel(const float* __restrict__ src, int64_t E, int c,
                                                                   uint8_t* __restrict__ out,
                                                                   float* __restrict__ scale) {
@@ -36,7 +30,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_fp8_kernel(const float* _
       const float4 x = row[q];
       amax = fmaxf(amax, fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
     }
-    amax = wave_max(amax);
+    amax = wave_max_f32(amax);          // in registers: DPP and lane swaps
     const float s = amax > 0.f ? amax / 448.0f : 1.0f;
     uint32_t* orow = reinterpret_cast<uint32_t*>(out + e * c);
     for (int q = lane; q < nq; q += 64) {

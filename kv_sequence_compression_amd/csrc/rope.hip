@@ -26,12 +26,6 @@ namespace {
 
 constexpr int kRopeThreads = 256;
 
-__device__ __forceinline__ float wave_max_f(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
-  return x;
-}
-
 // Angle of pair `kp` at position `pos`, reduced to [-pi, pi] in double
 // precision (positions of 10^6 tokens and more keep their accuracy), then
 // sin / cos in single precision.
@@ -120,7 +114,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_store_kernel(
         if (ch0 < cn)
 #pragma unroll
           for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[g][j]));
-        amax = wave_max_f(amax);
+        amax = wave_max_f32(amax);
         const float s = amax > 0.f ? amax / 448.0f : 1.0f;
         const bool store = k0 + g < ne && slot[g] >= 0 && slot[g] < n_slots;   // out-of-range rows are not stored
         if (store && lane == 0) scale[slot[g]] = s;
@@ -148,7 +142,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_store_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[j]));
     }
-    amax = wave_max_f(amax);
+    amax = wave_max_f32(amax);
     const float s = amax > 0.f ? amax / 448.0f : 1.0f;
     if (store && lane == 0) scale[slot] = s;
     const double pos = base_pos + (double)k * m;
