@@ -51,8 +51,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_tiles_kernel(const int64_t*
     const int base_tile = s_base_tile, base_ent = s_base_ent;
     // Cooperative write: tile k of this chunk belongs to the first sequence
     // whose inclusive tile prefix exceeds k.
+    const int n_seq = min(kPlanThreads, batch - b0);      // sequences of this chunk
     for (int k = tid; k < chunk_tiles; k += kPlanThreads) {
-      int lo = 0, hi = kPlanThreads - 1;
+      int lo = 0, hi = n_seq - 1;
       while (lo < hi) {
         const int mid = (lo + hi) >> 1;
         if (s_tile_end[mid] > k) hi = mid; else lo = mid + 1;
