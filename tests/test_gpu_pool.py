@@ -150,3 +150,19 @@ def test_pool_long_context_full_size_sampled(gpu_device):
         s = {nm: to64(st32[nm][lo:(i + 1) * 4]) for nm in st32}
         ref = oracle.csa_pool_sequence(s["Ca"], s["Cb"], s["Za"], s["Zb"], Ba, Bb, 4, i - lo // 4, i - lo // 4 + 1)
         assert max_abs_err(got[k:k + 1], ref) <= 1e-5, i
+
+
+def test_offsets_of_equal_size_are_not_confused(gpu_device):
+    """The binding keeps small device copies of the sequence offsets by
+    content: two layouts with the same number of sequences, called in turn
+    and then again, each give their own oracle result."""
+    case = _dev(synth.pool_case(1200, 32, m_csa=4, m_hca=8, seed=2, dtype="f32", bias_std=0.5, z_std=2.0),
+                gpu_device)
+    st = case.streams
+    layouts = [np.array([0, 400, 1200]), np.array([0, 804, 1200]), np.array([0, 400, 1200])]
+    for cu in layouts:
+        out, _ = sc.pool_csa(st["Ca"], st["Cb"], st["Za"], st["Zb"], case.biases["Ba"], case.biases["Bb"], 4, cu,
+                             "f32")
+        ref = _oracle_csa(case, cu)
+        assert out.shape == ref.shape
+        assert max_abs_err(to64(out), ref) <= 1e-5
