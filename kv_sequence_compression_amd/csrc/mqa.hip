@@ -361,21 +361,18 @@ __global__ __launch_bounds__(kMqThreads, 1) void mqa_sink_kernel(MqArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) poff[ks] = (uint32_t)((lane & 31) * 128 + (((2 * ks + h2) ^ ps) << 4));
     }
-    // Transposed entry fragments (A operand of the value product) of step ks
-    // (entries 16 ks ..) of tile buffer E, 8 entries of one column per lane:
-    // gfx950's transposing LDS read, 4 entries per read.
-    const auto load_et = [&](const char* E, int ks, bf16x8_t (&f)[4]) {
+    // Transposed entry fragment (A operand of the value product) of step ks
+    // (entries 16 ks ..) and column block cb of tile buffer E, 8 entries of
+    // one column per lane: gfx950's transposing LDS read, 4 entries per read.
+    const auto load_et_cb = [&](const char* E, int ks, int cb, bf16x8_t& f) {
       typedef short v4s __attribute__((ext_vector_type(4)));
+      v4s part[2];
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        v4s part[2];
-#pragma unroll
-        for (int half = 0; half < 2; ++half)
-          part[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) v4s*)(E + troff[half][cb] + 16 * kMqRowBytes * ks));
-        const uint2 lo = __builtin_bit_cast(uint2, part[0]), hi = __builtin_bit_cast(uint2, part[1]);
-        f[cb] = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
-      }
+      for (int half = 0; half < 2; ++half)
+        part[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s*)(E + troff[half][cb] + 16 * kMqRowBytes * ks));
+      const uint2 lo = __builtin_bit_cast(uint2, part[0]), hi = __builtin_bit_cast(uint2, part[1]);
+      f = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
     };
     const auto load_p = [&](const char* Pb, int ks, bf16x8_t (&f)[2]) {
 #pragma unroll
@@ -383,8 +380,9 @@ __global__ __launch_bounds__(kMqThreads, 1) void mqa_sink_kernel(MqArgs a) {
         f[hb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(Pb + poff[ks] + 32 * 128 * hb));
     };
     // O^T[col][head] += E^T[col][entry] P^T[entry][head] over one tile, from
-    // its fragments et and probabilities in Pb; with E_next, each step's
-    // fragments are replaced by the next tile's once its MFMAs are issued.
+    // its fragments et and probabilities in Pb; with refill, each fragment is
+    // replaced by the next tile's (from E_next) as soon as its two MFMAs are
+    // issued, so the transposing reads spread over the MFMAs.
     bf16x8_t et[4][4];
     const auto value_tile = [&](const char* Pb, const char* E_next, auto refill) {
       bf16x8_t bp[4][2];
@@ -393,12 +391,13 @@ __global__ __launch_bounds__(kMqThreads, 1) void mqa_sink_kernel(MqArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
+        for (int cb = 0; cb < 4; ++cb) {
 #pragma unroll
           for (int hb = 0; hb < 2; ++hb)
             o[cb][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(et[ks][cb], bp[ks][hb], o[cb][hb], 0, 0, 0);
-        if constexpr (decltype(refill)::value) load_et(E_next, ks, et[ks]);
-        __builtin_amdgcn_sched_barrier(0);
+          if constexpr (decltype(refill)::value) load_et_cb(E_next, ks, cb, et[ks][cb]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     };
 
@@ -411,7 +410,9 @@ __global__ __launch_bounds__(kMqThreads, 1) void mqa_sink_kernel(MqArgs a) {
         lds_barrier();                    // B: tile 0 in
         lds_barrier();                    // B: (the score waves' maxima)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) load_et(lds, ks, et[ks]);
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) load_et_cb(lds, ks, cb, et[ks][cb]);
         wait_lgkmcnt0();                  // tile 0's fragments read: its buffer may be refilled
         lds_barrier();                    // B: step 1 may start
 #pragma unroll 1
