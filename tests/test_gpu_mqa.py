@@ -85,6 +85,22 @@ def test_mqa_growing_logits_restart(gpu_device):
         check_mqa(to64(out), O, A, out_dtype, to64(lse), L)
 
 
+def test_mqa_restart_at_the_last_step(gpu_device):
+    """Logits that rise by about 1.5 (log2 units) per entry in half the heads:
+    from entry ~105 on, the second tile exceeds the first tile's maximum by
+    more than 64, so the two-tile sweeps (110 and 128 visible) restart at their
+    last step, just before the value product of the last tile, and the
+    five-tile sweep restarts again at later tiles.  One-tile sweeps (64, and 65
+    with a one-entry second tile) do not restart; sink with value."""
+    case = synth.mqa_case([5], [300], seed=4, device=gpu_device)
+    case.kv[:, 0] = (2.0 * torch.arange(300, device=gpu_device, dtype=torch.float32)).to(torch.bfloat16)
+    case.q[:, :64, 0] = 12.0
+    nv = np.array([110, 128, 64, 300, 65], dtype=np.int32)
+    out, lse = _run(case, nv, "key+value", "f32")
+    O, L, A = _ref(case, nv, np.arange(5), "key+value")
+    check_mqa(to64(out), O, A, "f32", to64(lse), L)
+
+
 def test_mqa_full_config_sampled(gpu_device):
     """HCA at 1M context: 8192 entries (2^20 tokens, m' = 128); the last 4096
     tokens attend with causal visibility; sink with value; bf16 out.  Sampled
