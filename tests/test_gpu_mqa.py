@@ -101,6 +101,22 @@ def test_mqa_restart_at_the_last_step(gpu_device):
     check_mqa(to64(out), O, A, "f32", to64(lse), L)
 
 
+def test_mqa_defaults_match_explicit_arguments(gpu_device):
+    """Omitted visible counts mean every entry of the query's sequence, the
+    default scale is 1/sqrt(512), and leaving out the log-sum-exp changes
+    nothing else: the outputs equal the explicit call's bit for bit, and the
+    oracle's within the usual bound."""
+    case = synth.mqa_case([3, 2], [150, 64], seed=6, device=gpu_device)
+    full = np.array([150] * 3 + [64] * 2, dtype=np.int32)
+    a, la = sc.shared_kv_mqa(case.q, case.kv, case.cu_q, case.cu_k, full, case.k_sink, case.v_sink, SCALE, "f32",
+                             with_lse=True)
+    b, lb = sc.shared_kv_mqa(case.q, case.kv, case.cu_q, case.cu_k, None, case.k_sink, case.v_sink, None, "f32")
+    assert lb is None
+    assert torch.equal(a, b)
+    O, L, A = _ref(case, full, np.arange(5), "key+value")
+    check_mqa(to64(b), O, A, "f32", to64(la), L)
+
+
 def test_mqa_full_config_sampled(gpu_device):
     """HCA at 1M context: 8192 entries (2^20 tokens, m' = 128); the last 4096
     tokens attend with causal visibility; sink with value; bf16 out.  Sampled
