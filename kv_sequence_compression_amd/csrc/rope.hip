@@ -64,6 +64,25 @@ __device__ __forceinline__ void store_chunk(const float (&x)[8], int ch0, int cn
 // loads in flight together; wave w takes entries G w + g, G w + g + 4 G, ...
 // Larger c: one entry at a time, 8 channels 8 l + 512 j per lane, two passes
 // over the row (the second hits the cache).
+// Entries are read exactly once: non-temporal 16-byte loads.
+typedef unsigned int rope_u32x4_t __attribute__((ext_vector_type(4)));
+template <int DIN>
+__device__ __forceinline__ void load8_stream(const char* p, float (&x)[8]) {
+  const rope_u32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const rope_u32x4_t*>(p));
+  if (DIN == DT_BF16) {
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+    const rope_u32x4_t b = __builtin_nontemporal_load(reinterpret_cast<const rope_u32x4_t*>(p + 16));
+    x[0] = __uint_as_float(a.x); x[1] = __uint_as_float(a.y); x[2] = __uint_as_float(a.z); x[3] = __uint_as_float(a.w);
+    x[4] = __uint_as_float(b.x); x[5] = __uint_as_float(b.y); x[6] = __uint_as_float(b.z); x[7] = __uint_as_float(b.w);
+  }
+}
+
 template <int DIN>
 __global__ __launch_bounds__(kRopeThreads) void rope_store_kernel(
     const char* __restrict__ entries, int c, int m, const int64_t* __restrict__ cu, const int64_t* __restrict__ pos0,
@@ -99,7 +118,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_store_kernel(
         const int k = min(k0 + g, ne - 1);                // past the tile end: re-read the last entry, store nothing
         const int64_t e = (int64_t)t.entry_start + k;
         slot[g] = slots ? slots[e] : e;
-        if (active) load8<DIN>(entries + (e * c + ch0) * ES, x[g]);
+        if (active) load8_stream<DIN>(entries + (e * c + ch0) * ES, x[g]);
         else
 #pragma unroll
           for (int j = 0; j < 8; ++j) x[g][j] = 0.f;
