@@ -14,10 +14,19 @@ Prints ONE JSON line (rank 0).  `value` is compressed entries/s of the step
 * roofline of the dominant kernel (the fused CSA call: MFMA-bound; its
   FLOPs are 2 * T * d * 4c per launch), timed with HIP events on the
   library's stream over the timed region;
+* csa_full (one sequence of 8192 tokens, 2048 entries) and hca_full (one
+  sequence of 131072 tokens, 1024 entries), each with its own roofline, the
+  projection alone and the unfused project-then-pool path beside it;
 * the pooling-only path on the long-context streams (four bf16 streams of
   2^20 x 512; CSA m=4 and HCA m'=128), HBM-bound;
+* the next-row kernels (indexer keys, decode append, RoPE store, lightning
+  indexer, HCA dense attention);
 * cpu_baseline: the float64 oracle on a bounded sample of the same workload
-  (the first 262144 tokens of the batch), on this host's cores.
+  (the first 262144 tokens of the batch) on this host's cores, the same on
+  one core, and per workload (tiny, csa_full, hca_full, pooling) with all
+  cores and with one; the host CPU model is recorded.
+
+--legs selects measurements (e.g. for a profiler run of one kernel).
 """
 
 from __future__ import annotations
@@ -72,6 +81,64 @@ def _blas_threads() -> int:
         return os.cpu_count() or 1
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _host_cores() -> int:
+    """Cores this process may run on (its affinity set), else os.cpu_count()."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
+
+
+def _time_calls(torch, calls, steps: int, warmup: int = 2):
+    """Median, minimum and mean time (ms) of one call, each call bracketed by
+    HIP events on the current stream (the stream the library launches on).
+    `calls` is one callable or a list that is cycled through (rotating input
+    sets)."""
+    calls = calls if isinstance(calls, (list, tuple)) else [calls]
+    for k in range(max(warmup, len(calls))):
+        calls[k % len(calls)]()
+    torch.cuda.synchronize()
+    ev = _events(torch, 2 * steps)
+    for k in range(steps):
+        ev[2 * k].record()
+        calls[k % len(calls)]()
+        ev[2 * k + 1].record()
+    torch.cuda.synchronize()
+    t = np.array([ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(steps)])
+    return float(np.median(t)), float(t.min()), float(t.mean())
+
+
+def _mfma_roofline(flops: float, ms: float, kernel: str, traffic_key=None):
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": tf / PEAK_BF16_TFLOPS, "traffic": _traffic(traffic_key) if traffic_key else None,
+            "kernel": kernel, "algorithmic_flops_per_launch": flops}
+
+
+def _oracle_rate(fn, threads):
+    """Seconds of fn() with the BLAS pool limited to `threads` (None: as is)."""
+    from threadpoolctl import threadpool_limits
+    if threads is None:
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+    with threadpool_limits(limits=threads):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+
 def cpu_baseline(case_csa, case_hca, sample_tokens: int):
     """The float64 oracle, as it stands, on the first `sample_tokens` tokens
     (whole sequences first, the last one truncated to a multiple of 128)."""
@@ -103,6 +170,119 @@ def cpu_baseline(case_csa, case_hca, sample_tokens: int):
     return {"value": entries / dt, "unit": "entries/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {tokens} tokens of the batch ({len(seqs)} sequence(s)); float64 numpy oracle; "
                       f"{dt:.2f} s; {tokens / dt:.1f} tokens/s"}
+
+
+def _f64(torch, t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def csa_full_leg(sc, synth, torch, steps, cpu: bool):
+    """CSA full workload: one sequence of 8192 tokens, d = 7168, c = 512,
+    m = 4 -> 2048 entries, bf16 out.  Its hidden states (117 MB) would sit in
+    the 256 MB last-level cache between calls, so three input sets are
+    rotated; the weights are the same for every call, as in use.  Also timed:
+    the projection alone (Y = H Wt^T, 8192 x 2048 bf16) and the unfused path
+    (that projection, then CSA pooling of its column slices)."""
+    cfg = synth.CONFIGS["csa_full"]
+    dev = torch.device("cuda:0")
+    T, d, c, m = cfg["lengths"][0], cfg["d"], cfg["c"], cfg["m"]
+    case = synth.compressor_case("csa", cfg["lengths"], d, c, m, seed=0, in_dtype="bf16", bias_std=cfg["bias_std"],
+                                 device=dev)
+    Hs = [case.H] + [synth.normal((T, d), 1.0, (k, synth.TID["H"]), dev, "bf16") for k in (1, 2)]
+    b = case.biases
+    fused = [lambda H=H: sc.compress_fused("csa", H, case.Wt_cat, b["Ba"], b["Bb"], m, case.cu_seqlens, "bf16")
+             for H in Hs]
+    Y = torch.empty((T, 4 * c), dtype=torch.bfloat16, device=dev)
+    proj = [lambda H=H: sc.project(H, case.Wt_cat, "bf16", out=Y) for H in Hs]
+
+    def unfused_call(H):
+        sc.project(H, case.Wt_cat, "bf16", out=Y)
+        sc.pool_csa(Y[:, :c], Y[:, c:2 * c], Y[:, 2 * c:3 * c], Y[:, 3 * c:], b["Ba"], b["Bb"], m, case.cu_seqlens,
+                    "bf16")
+    unfused = [lambda H=H: unfused_call(H) for H in Hs]
+    med, mn, mean = _time_calls(torch, fused, steps)
+    pmed, pmn, _ = _time_calls(torch, proj, steps)
+    umed, umn, _ = _time_calls(torch, unfused, steps)
+    flops = 2.0 * T * d * 4 * c
+    E = T // m
+    res = {"workload": f"csa_full: one sequence, n={T}, d={d}, c={c}, m={m} -> {E} entries, bf16 in/out "
+                       "(3 rotating hidden-state sets)",
+           "ms_median": med, "ms_min": mn, "entries_per_s": E / (med * 1e-3), "tokens_per_s": T / (med * 1e-3),
+           "roofline": _mfma_roofline(flops, med, "fused CSA call (planner + tile kernel + halo fix-up)",
+                                      "fused_csa_full"),
+           "project_alone": {"ms_median": pmed, "ms_min": pmn,
+                             "roofline": _mfma_roofline(flops, pmed, "seqcomp_project, 8192 x 2048 bf16 out",
+                                                        "project_csa_full")},
+           "unfused": {"ms_median": umed, "ms_min": umn, "entries_per_s": E / (umed * 1e-3),
+                       "fused_speedup": umed / med,
+                       "path": "seqcomp_project to bf16 [T x 4c], then seqcomp_pool_csa on its column slices"}}
+    if cpu:
+        import oracle
+        ne = 256                                            # first 256 entries: 1024 tokens
+        H = _f64(torch, case.H[:ne * m])
+        W = {k: _f64(torch, v) for k, v in case.W.items()}
+        bb = {k: _f64(torch, v) for k, v in b.items()}
+        run = lambda: oracle.csa_compress_sequence(H, W["W_KVa"], W["W_KVb"], W["W_Za"], W["W_Zb"], bb["Ba"],
+                                                   bb["Bb"], m)
+        res["cpu_oracle"] = _oracle_legs(run, ne, ne * m, f"first {ne} entries ({ne * m} tokens)")
+    del case, Hs, Y
+    torch.cuda.empty_cache()
+    return res
+
+
+def hca_full_leg(sc, synth, torch, steps, cpu: bool):
+    """HCA workload: one sequence of 131072 tokens, d = 7168, c = 512,
+    m' = 128 -> 1024 entries, bf16 out (hidden states 1.9 GB, far past the
+    last-level cache).  Also the projection alone and the unfused path."""
+    cfg = synth.CONFIGS["hca_full"]
+    dev = torch.device("cuda:0")
+    T, d, c, m = cfg["lengths"][0], cfg["d"], cfg["c"], cfg["m"]
+    case = synth.compressor_case("hca", cfg["lengths"], d, c, m, seed=0, in_dtype="bf16", bias_std=cfg["bias_std"],
+                                 device=dev)
+    B = case.biases["B"]
+    fused = lambda: sc.compress_fused("hca", case.H, case.Wt_cat, B, None, m, case.cu_seqlens, "bf16")
+    Y = torch.empty((T, 2 * c), dtype=torch.bfloat16, device=dev)
+    proj = lambda: sc.project(case.H, case.Wt_cat, "bf16", out=Y)
+
+    def unfused():
+        proj()
+        sc.pool_hca(Y[:, :c], Y[:, c:], B, m, case.cu_seqlens, "bf16")
+    med, mn, _ = _time_calls(torch, fused, steps)
+    pmed, pmn, _ = _time_calls(torch, proj, steps)
+    umed, umn, _ = _time_calls(torch, unfused, steps)
+    flops = 2.0 * T * d * 2 * c
+    E = T // m
+    res = {"workload": f"hca_full: one sequence, n={T}, d={d}, c={c}, m'={m} -> {E} entries, bf16 in/out",
+           "ms_median": med, "ms_min": mn, "entries_per_s": E / (med * 1e-3), "tokens_per_s": T / (med * 1e-3),
+           "roofline": _mfma_roofline(flops, med, "fused HCA call (planner + tile kernel)", "fused_hca_full"),
+           "project_alone": {"ms_median": pmed, "ms_min": pmn,
+                             "roofline": _mfma_roofline(flops, pmed, "seqcomp_project, 131072 x 1024 bf16 out",
+                                                        "project_hca_full")},
+           "unfused": {"ms_median": umed, "ms_min": umn, "entries_per_s": E / (umed * 1e-3),
+                       "fused_speedup": umed / med,
+                       "path": "seqcomp_project to bf16 [T x 2c], then seqcomp_pool_hca on its column slices"}}
+    if cpu:
+        import oracle
+        ne = 16                                             # first 16 entries: 2048 tokens
+        H = _f64(torch, case.H[:ne * m])
+        W = {k: _f64(torch, v) for k, v in case.W.items()}
+        Bh = _f64(torch, B)
+        run = lambda: oracle.hca_compress_sequence(H, W["W_KV"], W["W_Z"], Bh, m)
+        res["cpu_oracle"] = _oracle_legs(run, ne, ne * m, f"first {ne} entries ({ne * m} tokens)")
+    del case, Y
+    torch.cuda.empty_cache()
+    return res
+
+
+def _oracle_legs(run, entries: int, tokens: int, sample: str):
+    """The oracle on a sample, with every thread of its BLAS pool (the host
+    cores this process is given) and with one."""
+    out = {"kind": "oracle", "sample": sample, "cpu_model": _cpu_model()}
+    for name, threads in (("all_cores", None), ("one_core", 1)):
+        dt = _oracle_rate(run, threads)
+        out[name] = {"cores": _blas_threads() if threads is None else threads, "seconds": dt,
+                     "entries_per_s": entries / dt, "tokens_per_s": tokens / dt}
+    return out
 
 
 def indexer_keys(sc, synth, torch, csa, lengths, steps):
@@ -281,6 +461,42 @@ def hca_attention(sc, synth, torch, steps, cpu_queries=2):
     return res
 
 
+LEGS = ("step", "csa_full", "hca_full", "pool", "indexer_keys", "decode_append", "rope_store", "lightning_indexer",
+        "hca_attention")
+
+
+def tiny_cpu_oracle(synth, torch):
+    """The oracle on the whole tiny CSA workload (n = 64, d = 64, c = 32,
+    m = 4), repeated for a measurable time."""
+    import oracle
+    cfg = synth.CONFIGS["csa_tiny"]
+    case = synth.compressor_case("csa", cfg["lengths"], cfg["d"], cfg["c"], cfg["m"], seed=0, in_dtype="f32",
+                                 bias_std=cfg["bias_std"], device="cpu")
+    H = _f64(torch, case.H)
+    W = {k: _f64(torch, v) for k, v in case.W.items()}
+    b = {k: _f64(torch, v) for k, v in case.biases.items()}
+    reps = 200
+
+    def run():
+        for _ in range(reps):
+            oracle.csa_compress(H, W["W_KVa"], W["W_KVb"], W["W_Za"], W["W_Zb"], b["Ba"], b["Bb"], 4, case.cu_seqlens)
+    return _oracle_legs(run, 16 * reps, 64 * reps, f"the whole workload (16 entries) x {reps}")
+
+
+def pool_cpu_oracle(torch, pc):
+    """The oracle's pooling on the first 4096 CSA entries (16384 rows) and the
+    first 128 HCA entries (16384 rows) of the long-context streams."""
+    import oracle
+    rows = 16384
+    st = {k: _f64(torch, v[:rows]) for k, v in pc.streams.items()}
+    b = {k: _f64(torch, v) for k, v in pc.biases.items()}
+    csa = _oracle_legs(lambda: oracle.csa_pool_sequence(st["Ca"], st["Cb"], st["Za"], st["Zb"], b["Ba"], b["Bb"], 4),
+                       rows // 4, rows, f"first {rows // 4} CSA entries ({rows} rows of 4 streams)")
+    hca = _oracle_legs(lambda: oracle.hca_pool_sequence(st["Ca"], st["Za"], b["B"], 128),
+                       rows // 128, rows, f"first {rows // 128} HCA entries ({rows} rows of 2 streams)")
+    return {"csa": csa, "hca": hca}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -288,10 +504,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--pool-steps", type=int, default=20)
     ap.add_argument("--cpu-sample-tokens", type=int, default=262144)
+    ap.add_argument("--cpu-one-core-tokens", type=int, default=16384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-pool", action="store_true")
+    ap.add_argument("--legs", default=",".join(LEGS),
+                    help="comma-separated measurements to run (default: all): " + ", ".join(LEGS))
+    ap.add_argument("--no-pool", action="store_true", help="same as leaving 'pool' out of --legs")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the indexer-key compressor, decode-append, RoPE-store, lightning-indexer and "
+                    help="leave out the indexer-key compressor, decode-append, RoPE-store, lightning-indexer and "
                          "HCA-attention measurements")
     ap.add_argument("--profile-copy", action="store_true",
                     help="first run a plain 1 GiB device copy (torch copy kernel): the known-size reference that "
@@ -301,6 +520,17 @@ def main():
         print("bench.py measures one GPU only: this compressor build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    legs = [x for x in args.legs.split(",") if x]
+    unknown = set(legs) - set(LEGS)
+    if unknown:
+        print(f"unknown legs: {sorted(unknown)}", file=sys.stderr)
+        sys.exit(2)
+    if args.no_pool:
+        legs = [x for x in legs if x != "pool"]
+    if args.no_extras:
+        legs = [x for x in legs if x not in ("indexer_keys", "decode_append", "rope_store", "lightning_indexer",
+                                             "hca_attention")]
+    cpu = not args.no_cpu_baseline
 
     import torch
     import kv_sequence_compression_amd as sc
@@ -318,62 +548,63 @@ def main():
     lengths = synth.varlen_config_lengths(0)
     T = int(lengths.sum())
     d, c = cfg["d"], cfg["c"]
-    common = dict(seed=0, in_dtype="bf16", bias_std=cfg["bias_std"], device=dev,
-                  z_outlier_frac=cfg["z_outlier_frac"], z_outlier_scale=cfg["z_outlier_scale"])
-    csa = synth.compressor_case("csa", lengths, d, c, cfg["m_csa"], per_sequence_h=True, **common)
-    hca = synth.compressor_case("hca", lengths, d, c, cfg["m_hca"], H=csa.H, **common)   # same hidden states
-    E_csa, E_hca = csa.n_entries, hca.n_entries
-    bc, bh = csa.biases, hca.biases
+    out = {"metric": METRIC, "value": None, "unit": "entries/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "varlen_fp8: fused CSA (m=4) + fused HCA (m'=128) over 32 packed sequences, "
+                                  f"T={T}, d={d}, c={c}, fp8 E4M3 entries + per-entry fp32 scales",
+                      "tokens": T, "seq_lengths": "U[4096,65536] step 128"}}
+    need_varlen = any(x in legs for x in ("step", "indexer_keys", "decode_append", "rope_store"))
+    if need_varlen:
+        common = dict(seed=0, in_dtype="bf16", bias_std=cfg["bias_std"], device=dev,
+                      z_outlier_frac=cfg["z_outlier_frac"], z_outlier_scale=cfg["z_outlier_scale"])
+        csa = synth.compressor_case("csa", lengths, d, c, cfg["m_csa"], per_sequence_h=True, **common)
+        hca = synth.compressor_case("hca", lengths, d, c, cfg["m_hca"], H=csa.H, **common)   # same hidden states
+        E_csa, E_hca = csa.n_entries, hca.n_entries
+        bc, bh = csa.biases, hca.biases
+        out["config"].update({"entries_csa": E_csa, "entries_hca": E_hca})
 
-    def step():
-        sc.compress_fused("csa", csa.H, csa.Wt_cat, bc["Ba"], bc["Bb"], 4, csa.cu_seqlens, "fp8")
-        sc.compress_fused("hca", hca.H, hca.Wt_cat, bh["B"], None, 128, hca.cu_seqlens, "fp8")
+    if "step" in legs:
+        def step():
+            sc.compress_fused("csa", csa.H, csa.Wt_cat, bc["Ba"], bc["Bb"], 4, csa.cu_seqlens, "fp8")
+            sc.compress_fused("hca", hca.H, hca.Wt_cat, bh["B"], None, 128, hca.cu_seqlens, "fp8")
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev = _events(torch, 3 * args.steps)
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        ev[3 * k].record()
-        sc.compress_fused("csa", csa.H, csa.Wt_cat, bc["Ba"], bc["Bb"], 4, csa.cu_seqlens, "fp8")
-        ev[3 * k + 1].record()
-        sc.compress_fused("hca", hca.H, hca.Wt_cat, bh["B"], None, 128, hca.cu_seqlens, "fp8")
-        ev[3 * k + 2].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    csa_ms = float(np.mean([ev[3 * k].elapsed_time(ev[3 * k + 1]) for k in range(args.steps)]))
-    hca_ms = float(np.mean([ev[3 * k + 1].elapsed_time(ev[3 * k + 2]) for k in range(args.steps)]))
-    ms_step = wall * 1e3 / args.steps
-    flops_csa = 2.0 * T * d * 4 * c
-    flops_hca = 2.0 * T * d * 2 * c
-    achieved = flops_csa / (csa_ms * 1e-3) / 1e12
-    out = {
-        "metric": METRIC,
-        "value": (E_csa + E_hca) / (ms_step * 1e-3),
-        "unit": "entries/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "varlen_fp8: fused CSA (m=4) + fused HCA (m'=128) over 32 packed sequences, "
-                               f"T={T}, d={d}, c={c}, fp8 E4M3 entries + per-entry fp32 scales",
-                   "tokens": T, "entries_csa": E_csa, "entries_hca": E_hca, "seq_lengths": "U[4096,65536] step 128"},
-        "tokens_per_s": T / (ms_step * 1e-3),
-        "kernels_ms": {"fused_csa_call": csa_ms, "fused_hca_call": hca_ms},
-        "hca_roofline_frac": flops_hca / (hca_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": _traffic("fused_csa_varlen"),
-                     "kernel": "fused CSA call (tile kernel + planner + halo fix-up + fp8 encoder)",
-                     "algorithmic_flops_per_launch": flops_csa},
-    }
-    _progress("compressor step timed")
-    if not args.no_pool:
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        ev = _events(torch, 3 * args.steps)
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            ev[3 * k].record()
+            sc.compress_fused("csa", csa.H, csa.Wt_cat, bc["Ba"], bc["Bb"], 4, csa.cu_seqlens, "fp8")
+            ev[3 * k + 1].record()
+            sc.compress_fused("hca", hca.H, hca.Wt_cat, bh["B"], None, 128, hca.cu_seqlens, "fp8")
+            ev[3 * k + 2].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        csa_ms = float(np.mean([ev[3 * k].elapsed_time(ev[3 * k + 1]) for k in range(args.steps)]))
+        hca_ms = float(np.mean([ev[3 * k + 1].elapsed_time(ev[3 * k + 2]) for k in range(args.steps)]))
+        ms_step = wall * 1e3 / args.steps
+        flops_csa = 2.0 * T * d * 4 * c
+        flops_hca = 2.0 * T * d * 2 * c
+        out.update({
+            "value": (E_csa + E_hca) / (ms_step * 1e-3),
+            "ms_per_step": ms_step,
+            "tokens_per_s": T / (ms_step * 1e-3),
+            "kernels_ms": {"fused_csa_call": csa_ms, "fused_hca_call": hca_ms},
+            "hca_roofline_frac": flops_hca / (hca_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "roofline": _mfma_roofline(flops_csa, csa_ms,
+                                       "fused CSA call (tile kernel + planner + halo fix-up + fp8 encoder)",
+                                       "fused_csa_varlen"),
+        })
+        _progress("compressor step timed")
+    if "csa_full" in legs:
+        out["csa_full"] = csa_full_leg(sc, synth, torch, max(args.steps, 20), cpu)
+        _progress("CSA full workload measured")
+    if "hca_full" in legs:
+        out["hca_full"] = hca_full_leg(sc, synth, torch, max(args.steps, 10), cpu)
+        _progress("HCA workload measured")
+    if "pool" in legs:
         pc = synth.pool_case(1 << 20, 512, seed=0, dtype="bf16", device=dev, bias_std=0.02)
         st, pb = pc.streams, pc.biases
         n = 1 << 20
@@ -394,6 +625,7 @@ def main():
         bytes_csa = 4 * n * 512 * 2 + (n // 4) * 512 * 2
         bytes_hca = 2 * n * 512 * 2 + (n // 128) * 512 * 2
         gbs_csa = bytes_csa / (pcsa * 1e-3) / 1e9
+        gbs_hca = bytes_hca / (phca * 1e-3) / 1e9
         out["pool_only"] = {
             "workload": "pool_long: four bf16 streams of 1048576 x 512; CSA m=4 -> 262144 entries, "
                         "HCA m'=128 on (C^a, Z^a) -> 8192 entries; bf16 out",
@@ -403,27 +635,43 @@ def main():
             "roofline": {"bound": "hbm", "achieved": gbs_csa, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": gbs_csa / PEAK_HBM_GBS, "traffic": _traffic("pool_csa_long"),
                          "kernel": "CSA pooling call", "algorithmic_bytes_per_launch": bytes_csa},
-            "hca_roofline_frac": bytes_hca / (phca * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "hca_roofline": {"bound": "hbm", "achieved": gbs_hca, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": gbs_hca / PEAK_HBM_GBS, "traffic": _traffic("pool_hca_long"),
+                             "kernel": "HCA pooling call", "algorithmic_bytes_per_launch": bytes_hca},
+            "hca_roofline_frac": gbs_hca / PEAK_HBM_GBS,
         }
+        if cpu:
+            out["pool_only"]["cpu_oracle"] = pool_cpu_oracle(torch, pc)
         del pc, st
         torch.cuda.empty_cache()
-
-    if not args.no_pool:
         _progress("pooling-only path measured")
-    if not args.no_extras:
+    if "indexer_keys" in legs:
         out["indexer_keys"] = indexer_keys(sc, synth, torch, csa, lengths, args.steps)
         _progress("indexer-key compressor measured")
+    if "decode_append" in legs:
         out["decode_append"] = decode_append(sc, torch, csa, (64, 1024, 4096), args.steps)
         _progress("decode append measured")
+    if "rope_store" in legs:
         out["rope_store"] = rope_store(sc, torch, csa, args.steps)
         _progress("RoPE store measured")
+    if "lightning_indexer" in legs:
         out["lightning_indexer"] = lightning_indexer(sc, synth, torch, args.steps)
         _progress("lightning indexer measured")
+    if "hca_attention" in legs:
         out["hca_attention"] = hca_attention(sc, synth, torch, args.steps)
         _progress("HCA attention measured")
 
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(csa, hca, args.cpu_sample_tokens)
+    if cpu and "step" in legs:
+        base = cpu_baseline(csa, hca, args.cpu_sample_tokens)
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            one = cpu_baseline(csa, hca, args.cpu_one_core_tokens)
+        base["one_core"] = one
+        base["cpu_model"] = _cpu_model()
+        base["host_cores"] = _host_cores()
+        base["csa_tiny"] = tiny_cpu_oracle(synth, torch)
+        out["cpu_baseline"] = base
+        _progress("oracle baselines timed")
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -5,8 +5,12 @@ Tolerances (written per test):
   fp32 dot product of length d errs by at most ~d * 2^-24 * sum |h w|, which
   is below 2e-5 for these shapes; entries are convex combinations of such
   values, so max abs <= 2e-5;
-* bf16 operands (bf16 MFMA, fp32 accumulation): per-row relative <= 2e-2;
-* fp8 output: one E4M3 step on top of the bf16 path error (tests/helpers.py).
+* the tiny CSA workload (fp32, d = 64): max abs <= 1e-5, its stated bar;
+* bf16 operands (bf16 MFMA, fp32 accumulation): per-row relative <= 2e-2,
+  and <= 2^-8 for the fused path (see BF16_OBSERVED);
+* fp8 output: one E4M3 step on top of the bf16 path error (tests/helpers.py),
+  and the encoder's codes equal to the oracle encoder's on the kernel's own
+  fp32 entries except at rounding midpoints.
 """
 
 import numpy as np
@@ -16,9 +20,16 @@ import torch
 import oracle
 import kv_sequence_compression_amd as sc
 from kv_sequence_compression_amd import synth
-from helpers import to64, max_abs_err, row_rel_err, check_fp8, sample_entries, entry_owner
+from helpers import (to64, max_abs_err, row_rel_err, check_fp8, fused_round_xcd_samples, oracle_entries, fp8_codes_match_encoder)
 
 pytestmark = pytest.mark.gpu
+
+# A bf16-operand entry is an fp32-accumulated value rounded once to bf16
+# (relative 2^-9); the fp32 sums of exact bf16 products add ~1e-6.  The bf16
+# paths are held to the stated 2e-2 per-row bar AND to this 2^-8 bound of the
+# arithmetic itself, so that a logic error too small for 2e-2 (a dropped
+# bias of std 0.02 moves entries by ~1%) still fails.
+BF16_OBSERVED = 2.0 ** -8
 
 
 def _W64(case):
@@ -33,27 +44,6 @@ def _oracle_full(case):
         return oracle.csa_compress(H, W["W_KVa"], W["W_KVb"], W["W_Za"], W["W_Zb"], b["Ba"], b["Bb"], case.m,
                                    case.cu_seqlens)
     return oracle.hca_compress(H, W["W_KV"], W["W_Z"], b["B"], case.m, case.cu_seqlens)
-
-
-def _oracle_sampled(case, idx):
-    """Oracle value of the packed entries `idx`, projecting only the rows each reads."""
-    W = _W64(case)
-    b = {k: to64(v) for k, v in case.biases.items()}
-    seq, loc = entry_owner(case.cu_seqlens, case.m, idx)
-    rows = []
-    m = case.m
-    for s, i in zip(seq, loc):
-        t0 = int(case.cu_seqlens[s])
-        if case.mode == "csa":
-            lo = max(i - 1, 0) * m
-            H = to64(case.H[t0 + lo:t0 + (i + 1) * m])
-            k = i - lo // m
-            rows.append(oracle.csa_compress_sequence(H, W["W_KVa"], W["W_KVb"], W["W_Za"], W["W_Zb"], b["Ba"], b["Bb"],
-                                                     m, k, k + 1))
-        else:
-            H = to64(case.H[t0 + i * m:t0 + (i + 1) * m])
-            rows.append(oracle.hca_compress_sequence(H, W["W_KV"], W["W_Z"], b["B"], m))
-    return np.concatenate(rows)
 
 
 def _run(case, out_dtype):
@@ -106,14 +96,18 @@ def test_project_into_padded_rows(gpu_device, od):
 # -------------------------------------------------------------- fused, fp32
 
 def test_fused_csa_tiny_config(gpu_device):
-    """CSA tiny workload (n=64, d=64, c=32, m=4 -> 16 entries, fp32): max abs <= 2e-5."""
+    """CSA tiny workload (n=64, d=64, c=32, m=4 -> 16 entries, fp32 in and
+    out): max abs <= 1e-5, the bar stated for this workload.  An fp32 dot
+    product over d = 64 errs by ~1e-7 here; the observed error is printed."""
     cfg = synth.CONFIGS["csa_tiny"]
     case = synth.compressor_case("csa", cfg["lengths"], cfg["d"], cfg["c"], cfg["m"], seed=0, in_dtype="f32",
                                  bias_std=cfg["bias_std"], device=gpu_device)
     out, scale = _run(case, "f32")
     ref = _oracle_full(case)
     assert out.shape == (16, 32) and scale is None
-    assert max_abs_err(to64(out), ref) <= 2e-5
+    err = max_abs_err(to64(out), ref)
+    print(f"csa_tiny: max abs err {err:.3e} (bar 1e-5)")
+    assert err <= 1e-5
 
 
 @pytest.mark.parametrize("mode,lengths,d,c", [
@@ -143,15 +137,17 @@ def test_fused_zero_entries(gpu_device):
 
 @pytest.mark.parametrize("mode", ["csa", "hca"])
 def test_fused_bf16_matches_unfused(gpu_device, mode):
-    """bf16 fused vs the oracle (all entries) and vs the unfused path
-    (project, then pool on column slices): per-row relative <= 2e-2."""
+    """bf16 fused vs the oracle (all entries): per-row relative <= 2e-2 and
+    <= 2^-8 observed; the unfused path (project to bf16, then pool on column
+    slices; the bf16 rounding of the logits adds its own error): <= 2e-2."""
     lengths = [1000, 4, 777] if mode == "csa" else [1280, 200, 300]
     m = 4 if mode == "csa" else 128
     d, c = 256, 128
     case = synth.compressor_case(mode, lengths, d, c, m, seed=4, in_dtype="bf16", bias_std=0.3, device=gpu_device)
     ref = _oracle_full(case)
     out, _ = _run(case, "bf16")
-    assert row_rel_err(to64(out), ref).max() <= 2e-2
+    rel = row_rel_err(to64(out), ref)
+    assert rel.max() <= 2e-2 and rel.max() <= BF16_OBSERVED
     Y = sc.project(case.H, case.Wt_cat, "bf16")
     b = case.biases
     if mode == "csa":
@@ -162,42 +158,55 @@ def test_fused_bf16_matches_unfused(gpu_device, mode):
     assert row_rel_err(to64(un), ref).max() <= 2e-2
 
 
-def test_csa_full_config_sampled(gpu_device):
+def _n_cu(dev):
+    return torch.cuda.get_device_properties(dev).multi_processor_count
+
+
+def test_csa_full_config_all_entries(gpu_device):
     """CSA full workload: n=8192, d=7168, c=512, m=4 -> 2048 entries, bf16.
-    Sampled entries (every tile boundary of the first tiles, first, last,
-    random) against the oracle: per-row relative <= 2e-2."""
+    Every entry against the oracle (the launch is one persistent round of
+    256 tiles): per-row relative <= 2e-2, and <= 2^-8 observed."""
     cfg = synth.CONFIGS["csa_full"]
     case = synth.compressor_case("csa", cfg["lengths"], cfg["d"], cfg["c"], cfg["m"], seed=0,
                                  in_dtype="bf16", bias_std=cfg["bias_std"], device=gpu_device)
     out, _ = _run(case, "bf16")
     assert out.shape == (2048, 512)
-    idx = sample_entries(2048, 24, seed=9, must=(0, 1, 31, 32, 63, 64, 65, 127, 128, 2047))
-    ref = _oracle_sampled(case, idx)
-    got = to64(out[torch.from_numpy(idx).to(gpu_device)])
-    rel = row_rel_err(got, ref)
-    assert rel.max() <= 2e-2, rel.max()
+    ref = _oracle_full(case)
+    rel = row_rel_err(to64(out), ref)
+    print(f"csa_full: all 2048 entries, max per-row rel err {rel.max():.3e}")
+    assert rel.max() <= 2e-2
+    assert rel.max() <= BF16_OBSERVED
 
 
-def test_hca_full_config_sampled(gpu_device):
-    """HCA workload: n=131072, d=7168, c=512, m'=128 -> 1024 entries, bf16."""
+def test_hca_full_config_every_round_and_xcd(gpu_device):
+    """HCA workload: n=131072, d=7168, c=512, m'=128 -> 1024 entries, bf16.
+    Entries from every (persistent round, XCD) pair of the launch, and every
+    entry of the first and last rounds' tiles: per-row relative <= 2e-2 and
+    <= 2^-8 observed."""
     cfg = synth.CONFIGS["hca_full"]
     case = synth.compressor_case("hca", cfg["lengths"], cfg["d"], cfg["c"], cfg["m"], seed=0,
                                  in_dtype="bf16", bias_std=cfg["bias_std"], device=gpu_device)
     out, _ = _run(case, "bf16")
     assert out.shape == (1024, 512)
-    idx = sample_entries(1024, 6, seed=10, must=(0, 1, 2, 1023))
-    ref = _oracle_sampled(case, idx)
+    idx = fused_round_xcd_samples(case.cu_seqlens, case.m, "hca", case.c, _n_cu(gpu_device), seed=10)
+    ref = oracle_entries(case, idx)
     got = to64(out[torch.from_numpy(idx).to(gpu_device)])
-    assert row_rel_err(got, ref).max() <= 2e-2
+    rel = row_rel_err(got, ref)
+    print(f"hca_full: {idx.size} sampled entries, max per-row rel err {rel.max():.3e}")
+    assert rel.max() <= 2e-2
+    assert rel.max() <= BF16_OBSERVED
 
 
-def test_varlen_fp8_config_sampled(gpu_device):
+def test_varlen_fp8_config_every_round_and_xcd(gpu_device):
     """Batched variable-length workload: 32 sequences (lengths uniform in
     [4096, 65536] in steps of 128; seed 0 gives T = 968,960), d=7168, c=512,
     fused CSA (242,240 entries) and HCA (7,570 entries) with 1% of the Z
-    channels scaled x30, fp8 E4M3 output with per-entry scales.  Sampled
-    entries (each sequence's entry 0 and its first tile boundary, random):
-    scale within 2e-2 and one E4M3 step on top of 2e-2 * max |ref|."""
+    channels scaled x30, fp8 E4M3 output with per-entry scales.  Entries from
+    every (persistent round, XCD) pair of each launch, every tile boundary of
+    the first and last rounds and every sequence's entry 0: scale within 2e-2
+    and one E4M3 step on top of 2e-2 * max |ref|.  The same launch with fp32
+    output must give codes identical to the oracle's encoder on those fp32
+    entries (except at rounding midpoints)."""
     cfg = synth.CONFIGS["varlen_fp8"]
     lengths = synth.varlen_config_lengths(0)
     assert int(lengths.sum()) == 968960
@@ -211,10 +220,16 @@ def test_varlen_fp8_config_sampled(gpu_device):
         assert q.shape == (E, 512) and s.shape == (E,)
         counts = np.diff(case.cu_seqlens) // m
         starts = np.concatenate([[0], np.cumsum(counts)])[:-1]
-        must = list(starts) + (list(starts + 64) if mode == "csa" else [])   # entry 64: second tile of a sequence
-        idx = sample_entries(E, 16, seed=11, must=must)
-        ref = _oracle_sampled(case, idx)
+        idx = np.union1d(fused_round_xcd_samples(case.cu_seqlens, m, mode, case.c, _n_cu(gpu_device), seed=11),
+                         starts[counts > 0])
+        ref = oracle_entries(case, idx)
         sel = torch.from_numpy(idx).to(gpu_device)
-        check_fp8(q[sel], s[sel], ref, path_rel=2e-2)
-        del case, q, s
+        srel, excess = check_fp8(q[sel], s[sel], ref, path_rel=2e-2)
+        f32, _ = _run(case, "f32")
+        n, mids = fp8_codes_match_encoder(q[sel].cpu().numpy(), s[sel].cpu().numpy(), to64(f32[sel]))
+        rel = row_rel_err(to64(f32[sel]), ref)
+        print(f"varlen {mode}: {idx.size} sampled entries; fp32 entries max per-row rel err {rel.max():.3e}; "
+              f"fp8 scale rel err {srel:.3e}; {n} codes, {mids} at rounding midpoints")
+        assert rel.max() <= 2e-2 and rel.max() <= BF16_OBSERVED
+        del case, q, s, f32
         torch.cuda.empty_cache()

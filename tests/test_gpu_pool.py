@@ -12,7 +12,7 @@ import torch
 import oracle
 import kv_sequence_compression_amd as sc
 from kv_sequence_compression_amd import synth
-from helpers import to64, max_abs_err, row_rel_err, check_fp8, sample_entries, entry_owner
+from helpers import to64, max_abs_err, row_rel_err, check_fp8, sample_entries, fp8_codes_match_encoder
 
 pytestmark = pytest.mark.gpu
 
@@ -79,6 +79,35 @@ def test_pool_bf16_and_fp8_outputs(gpu_device):
     refh = _oracle_hca(case, cu)
     qh, sh = sc.pool_hca(st["Ca"], st["Za"], case.biases["B"], 128, cu, "fp8")
     check_fp8(qh, sh, refh, path_rel=0.0, path_abs=1e-5)
+
+
+def test_fp8_encoder_codes_match_oracle(gpu_device):
+    """The fp8 encoder alone: fp32 streams pooled to fp32 and to fp8 by the
+    same kernels; the codes must equal oracle.fp8_entry_quantize of the fp32
+    entries exactly (except within 1e-6 relative of a rounding midpoint,
+    where the two neighbours are allowed) and the scales must be within one
+    fp32 ulp of max |x| / 448.  Entries span magnitudes 1e-3 to 1e3, one is
+    all zero (scale 1, codes 0), and both CSA and HCA pooling are encoded."""
+    n, c = 4 * 700, 96
+    case = _dev(synth.pool_case(n, c, m_csa=4, m_hca=8, seed=7, dtype="f32", bias_std=0.5, z_std=2.0), gpu_device)
+    st = case.streams
+    mag = torch.from_numpy(10.0 ** np.random.default_rng(8).uniform(-3, 3, size=(n, 1))).float().to(gpu_device)
+    for k in ("Ca", "Cb"):
+        st[k] = (st[k] * mag).contiguous()
+    st["Ca"][4 * 9:4 * 10] = 0.0          # entry 9 reads a-rows of block 9 and b-rows of block 8
+    st["Cb"][4 * 8:4 * 9] = 0.0
+    st["Ca"][8 * 5:8 * 6] = 0.0           # HCA (m' = 8) entry 5 is all zero
+    b = case.biases
+    for pool, args in (("csa", (st["Ca"], st["Cb"], st["Za"], st["Zb"], b["Ba"], b["Bb"], 4)),
+                       ("hca", (st["Ca"], st["Za"], b["B"][:8].contiguous(), 8))):
+        fn = sc.pool_csa if pool == "csa" else sc.pool_hca
+        x, _ = fn(*args, None, "f32")
+        q, s = fn(*args, None, "fp8")
+        x64 = to64(x)
+        zero = 9 if pool == "csa" else 5
+        assert np.all(x64[zero] == 0) and float(s[zero]) == 1.0 and bool((q[zero] == 0).all())
+        n_codes, mids = fp8_codes_match_encoder(q.cpu().numpy(), s.cpu().numpy(), x64)
+        print(f"fp8 encoder ({pool} pool): {n_codes} codes identical to the oracle's, {mids} at rounding midpoints")
 
 
 def test_pool_weights_sum_to_one(gpu_device):
