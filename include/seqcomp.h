@@ -54,7 +54,10 @@
  * frees memory; scratch space comes from the caller's `workspace` (size from
  * seqcomp_workspace_bytes).  It keeps no state between calls and is safe to
  * call from several host threads on different streams, given disjoint
- * outputs and workspaces.
+ * outputs and workspaces.  The one exception is
+ * seqcomp_compress_fused_noalloc, which takes no workspace: it runs in a
+ * 64 MiB scratch array that the library holds per device, shared by all such
+ * calls on that device.
  *
  * Errors: every argument is validated on the host before any HIP call; on a
  * failed validation nothing is launched and no output is written.  A launch
@@ -82,7 +85,8 @@ enum seqcomp_status_code {
   SEQCOMP_E_WORKSPACE = 6,   /* workspace missing or smaller than required      */
   SEQCOMP_E_UNSUPPORTED = 7, /* well-formed but not supported (m, d, c)         */
   SEQCOMP_E_HIP = 8,         /* a HIP runtime call or kernel launch failed      */
-  SEQCOMP_E_SEQLENS = 9      /* cu_seqlens not 0-based / not non-decreasing / past T */
+  SEQCOMP_E_SEQLENS = 9,     /* cu_seqlens not 0-based / not non-decreasing / past T */
+  SEQCOMP_E_SCRATCH = 10     /* the allocation-free call needs more than its 64 MiB */
 };
 
 enum seqcomp_dtype { SEQCOMP_F32 = 0, SEQCOMP_BF16 = 1, SEQCOMP_FP8_E4M3 = 2 };
@@ -163,6 +167,29 @@ int seqcomp_compress_fused(int mode, int64_t m, const void* H, int64_t d, int in
                            const int64_t* cu_seqlens_host, const int64_t* cu_seqlens_dev, int64_t batch,
                            void* out, int out_dtype, float* out_scale,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Allocation-free form of seqcomp_compress_fused, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, computation and results
+ * as seqcomp_compress_fused, without the workspace: the call uses a 64 MiB
+ * scratch array that the library holds on each device it runs on (from the
+ * first such call on that device until the process ends).  It calls no
+ * allocator.
+ *   A call whose workspace would exceed 64 MiB (see seqcomp_workspace_bytes
+ *   with SEQCOMP_OP_FUSED) is rejected with SEQCOMP_E_SCRATCH before any
+ *   launch: at c = 512 that is about 5400 tiles of 256 rows (~1.38M tokens)
+ *   for CSA with bf16 or fp32 output, and about 470 tiles (~120K tokens)
+ *   with fp8 output, whose fp32 staging also lives there.
+ *   Every call on a device shares that device's array: calls that overlap in
+ *   time on one device (two streams, two host threads) race and may produce
+ *   wrong entries; serialise them.  Nothing in the array needs to start at
+ *   zero (each call writes what it later reads).
+ */
+int seqcomp_compress_fused_noalloc(int mode, int64_t m, const void* H, int64_t d, int in_dtype,
+                                   const void* Wt, int64_t c, const float* Ba, const float* Bb,
+                                   const int64_t* cu_seqlens_host, const int64_t* cu_seqlens_dev, int64_t batch,
+                                   void* out, int out_dtype, float* out_scale, void* stream);
 
 /*
  * CSA decode append: the compressor of eq. attn-seqcomp-csa-proj,

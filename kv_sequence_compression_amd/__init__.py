@@ -29,7 +29,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["SeqcompError", "project", "pool_csa", "pool_hca", "compress_fused", "csa_append", "csa_empty_state",
+__all__ = ["SeqcompError", "project", "pool_csa", "pool_hca", "compress_fused", "compress_fused_noalloc",
+           "csa_append", "csa_empty_state",
            "rope_store", "rope_cache", "num_entries", "workspace_bytes", "version", "lib"]
 
 _DT_CODE = {"f32": _lib.F32, "bf16": _lib.BF16, "fp8": _lib.FP8_E4M3}
@@ -225,6 +226,32 @@ def compress_fused(mode: str, H, Wt, Ba, Bb, m: int, cu_seqlens=None, out_dtype:
                                         _DT_CODE[out_dtype], _ptr(scale), _ptr(ws), ws_n, _stream(dev)),
            "seqcomp_compress_fused")
     return out, scale
+
+
+def compress_fused_noalloc(mode: str, H, Wt, Ba, Bb, m: int, cu_seqlens=None, out_dtype: str = "bf16", out=None,
+                           out_scale=None):
+    """compress_fused through the allocation-free entry point: the library
+    uses its own per-device scratch (64 MiB) instead of a workspace.  `out`
+    (and `out_scale` for fp8) may be passed pre-allocated; otherwise they are
+    allocated here, outside the library call."""
+    mcode = {"csa": _lib.MODE_CSA, "hca": _lib.MODE_HCA}[mode]
+    T, d = H.shape
+    S = 4 if mode == "csa" else 2
+    c = Wt.shape[0] // S
+    if Wt.shape != (S * c, d):
+        raise ValueError(f"Wt must be [{S}*c x d]")
+    dev = H.device
+    host, cu_dev = _cu_arrays([0, T] if cu_seqlens is None else cu_seqlens, dev)
+    E = num_entries(host, m)
+    if out is None:
+        out, out_scale = _alloc_out(E, c, out_dtype, dev)
+    elif out.shape != (E, c) or out.dtype != _TORCH_OUT[out_dtype] or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous [{E} x {c}] {_TORCH_OUT[out_dtype]} tensor")
+    _check(lib().seqcomp_compress_fused_noalloc(mcode, int(m), _ptr(H), d, _in_code(H), _ptr(Wt), c, _ptr(Ba),
+                                                _ptr(Bb), _i64p(host), _ptr(cu_dev), host.size - 1, _ptr(out),
+                                                _DT_CODE[out_dtype], _ptr(out_scale), _stream(dev)),
+           "seqcomp_compress_fused_noalloc")
+    return out, out_scale
 
 
 def csa_empty_state(nb: int, c: int, device) -> torch.Tensor:

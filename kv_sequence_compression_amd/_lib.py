@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libseqcomp.
 
 # Mirror of the enums in include/seqcomp.h.
 OK = 0
+E_SCRATCH = 10
 F32, BF16, FP8_E4M3 = 0, 1, 2
 MODE_CSA, MODE_HCA = 0, 1
 OP_POOL_CSA, OP_POOL_HCA, OP_FUSED = 0, 1, 2
@@ -36,6 +37,8 @@ SIGNATURES = {
                                   _i64p, _vp, _c_i64, _vp, _c_int, _vp, _vp, _size, _vp]),
     "seqcomp_compress_fused": (_c_int, [_c_int, _c_i64, _vp, _c_i64, _c_int, _vp, _c_i64, _vp, _vp,
                                         _i64p, _vp, _c_i64, _vp, _c_int, _vp, _vp, _size, _vp]),
+    "seqcomp_compress_fused_noalloc": (_c_int, [_c_int, _c_i64, _vp, _c_i64, _c_int, _vp, _c_i64, _vp, _vp,
+                                                _i64p, _vp, _c_i64, _vp, _c_int, _vp, _vp]),
     "seqcomp_csa_append": (_c_int, [_vp, _c_i64, _c_i64, _c_int, _vp, _c_i64, _vp, _vp, _vp, _vp,
                                     _vp, _c_int, _vp, _vp, _size, _vp]),
     "seqcomp_append_workspace_bytes": (_size, [_c_i64, _c_i64, _c_int]),

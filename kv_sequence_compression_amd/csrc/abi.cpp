@@ -8,6 +8,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "launch.hpp"
 
 using namespace seqcomp;
@@ -203,6 +205,99 @@ int pool_common(bool csa, const void* const* streams, int n_streams, int64_t ld_
                   static_cast<hipStream_t>(stream));
 }
 
+// Scratch of the allocation-free fused entry point: one array per device
+// (each device that loads the library holds its own copy until the process
+// ends).  Host code never uses the array's name as
+// an address: it is a host-side stand-in.  The device address comes from
+// hipGetSymbolAddress, once per device, and is kept in g_scratch.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// Device address of the current device's scratch array.
+int device_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SEQCOMP_E_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SEQCOMP_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SEQCOMP_E_HIP;
+    g_scratch[dev] = p;
+  }
+  *ptr = g_scratch[dev];
+  return SEQCOMP_OK;
+}
+
+// The fused compressor behind both entry points.  With use_scratch the
+// workspace arguments are ignored and the call runs in this device's
+// file-scope scratch array instead (rejected when it needs more).
+int fused_impl(int mode, int64_t m, const void* H, int64_t d, int in_dtype, const void* Wt, int64_t c,
+               const float* Ba, const float* Bb, const int64_t* cu_seqlens_host, const int64_t* cu_seqlens_dev,
+               int64_t batch, void* out, int out_dtype, float* out_scale, void* workspace, size_t workspace_bytes,
+               bool use_scratch, void* stream) {
+  if (mode != SEQCOMP_MODE_CSA && mode != SEQCOMP_MODE_HCA) return SEQCOMP_E_UNSUPPORTED;
+  const bool csa = mode == SEQCOMP_MODE_CSA;
+  if ((csa && m != 4) || (!csa && m != 128)) return SEQCOMP_E_UNSUPPORTED;
+  if (!valid_in_dtype(in_dtype)) return SEQCOMP_E_DTYPE;
+  if (!valid_out_dtype(out_dtype)) return SEQCOMP_E_DTYPE;
+  if (d < 64 || d % 64 != 0 || d > (int64_t(1) << 24)) return SEQCOMP_E_UNSUPPORTED;
+  if (c < 16 || c % 16 != 0 || c > (int64_t(1) << 20)) return SEQCOMP_E_UNSUPPORTED;
+  if (!csa && Bb) return SEQCOMP_E_SHAPE;
+  // the kernels address one 256-row tile of H and all of Wt with 32-bit byte offsets
+  if ((csa ? 4 : 2) * c * d * elt_size(in_dtype) >= (int64_t(1) << 32) ||
+      256 * d * elt_size(in_dtype) >= (int64_t(1) << 32))
+    return SEQCOMP_E_UNSUPPORTED;
+  int64_t T = 0;
+  int st = check_cu(cu_seqlens_host, batch, &T);
+  if (st) return st;
+  const int64_t E = entries_of(cu_seqlens_host, batch, m);
+  Range out_r, scale_r;
+  if ((st = check_output(out_dtype, out, out_scale, E, c, &out_r, &scale_r))) return st;
+  if (E == 0) return SEQCOMP_OK;
+  if (!H || !Wt || !Ba || (csa && !Bb) || !cu_seqlens_dev) return SEQCOMP_E_NULL;
+  if (!aligned16(H) || !aligned16(Wt) || !aligned16(Ba) || (csa && !aligned16(Bb)) || !aligned16(cu_seqlens_dev))
+    return SEQCOMP_E_ALIGN;
+  const WsLayout L = ws_layout(SEQCOMP_OP_FUSED, mode, m, c, cu_seqlens_host, batch, out_dtype);
+  if (use_scratch) {
+    // every check above is host-only; this is the call's first HIP call
+    if (L.total > kScratchBytes) return SEQCOMP_E_SCRATCH;
+    if ((st = device_scratch(&workspace))) return st;
+    workspace_bytes = kScratchBytes;
+  }
+  Range ws_r;
+  if ((st = check_workspace(workspace, workspace_bytes, L.total, &ws_r))) return st;
+  const int es = elt_size(in_dtype);
+  const int S = csa ? 4 : 2;
+  Range reads[5];
+  int nr = 0;
+  reads[nr++] = range_of(H, (size_t)T * d * es);
+  reads[nr++] = range_of(Wt, (size_t)S * c * d * es);
+  reads[nr++] = range_of(Ba, (size_t)m * c * 4);
+  if (csa) reads[nr++] = range_of(Bb, (size_t)m * c * 4);
+  reads[nr++] = range_of(cu_seqlens_dev, (size_t)(batch + 1) * 8);
+  const Range writes[3] = {out_r, scale_r, ws_r};
+  if ((st = check_alias(writes, 3, reads, nr))) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* wsb = static_cast<char*>(workspace);
+  TileRec* tiles = reinterpret_cast<TileRec*>(wsb + L.tiles_off);
+  float* halo = csa ? reinterpret_cast<float*>(wsb + L.halo_off) : nullptr;
+  const bool fp8 = out_dtype == SEQCOMP_FP8_E4M3;
+  void* dst = fp8 ? (void*)(wsb + L.stage_off) : out;
+  const int dst_dt = fp8 ? DT_F32 : out_dtype;
+  hipError_t e = launch_plan(cu_seqlens_dev, (int)batch, (int)m, kFusedTileRows, tiles, (int)L.n_tiles, s);
+  if (e == hipSuccess)
+    e = launch_fused(mode, in_dtype, dst_dt, H, (int)d, Wt, (int)c, Ba, Bb, tiles, (int)L.n_tiles, dst, halo, s);
+  if (e == hipSuccess && csa) e = launch_csa_fixup(dst_dt, tiles, (int)L.n_tiles, (int)c, halo, dst, s);
+  if (e == hipSuccess && fp8)
+    e = launch_quant_fp8(reinterpret_cast<const float*>(dst), E, (int)c, static_cast<uint8_t*>(out), out_scale, s);
+  return hip_status(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -221,6 +316,7 @@ const char* seqcomp_status_string(int status) {
     case SEQCOMP_E_UNSUPPORTED: return "configuration not supported (m, d or c)";
     case SEQCOMP_E_HIP: return "HIP runtime call or kernel launch failed";
     case SEQCOMP_E_SEQLENS: return "cu_seqlens must start at 0 and be non-decreasing";
+    case SEQCOMP_E_SCRATCH: return "the call needs more scratch than the allocation-free entry point holds (64 MiB)";
     default: return "unknown status";
   }
 }
@@ -287,57 +383,16 @@ int seqcomp_compress_fused(int mode, int64_t m, const void* H, int64_t d, int in
                            const float* Ba, const float* Bb, const int64_t* cu_seqlens_host,
                            const int64_t* cu_seqlens_dev, int64_t batch, void* out, int out_dtype,
                            float* out_scale, void* workspace, size_t workspace_bytes, void* stream) {
-  if (mode != SEQCOMP_MODE_CSA && mode != SEQCOMP_MODE_HCA) return SEQCOMP_E_UNSUPPORTED;
-  const bool csa = mode == SEQCOMP_MODE_CSA;
-  if ((csa && m != 4) || (!csa && m != 128)) return SEQCOMP_E_UNSUPPORTED;
-  if (!valid_in_dtype(in_dtype)) return SEQCOMP_E_DTYPE;
-  if (!valid_out_dtype(out_dtype)) return SEQCOMP_E_DTYPE;
-  if (d < 64 || d % 64 != 0 || d > (int64_t(1) << 24)) return SEQCOMP_E_UNSUPPORTED;
-  if (c < 16 || c % 16 != 0 || c > (int64_t(1) << 20)) return SEQCOMP_E_UNSUPPORTED;
-  if (!csa && Bb) return SEQCOMP_E_SHAPE;
-  // the kernels address one 256-row tile of H and all of Wt with 32-bit byte offsets
-  if ((csa ? 4 : 2) * c * d * elt_size(in_dtype) >= (int64_t(1) << 32) ||
-      256 * d * elt_size(in_dtype) >= (int64_t(1) << 32))
-    return SEQCOMP_E_UNSUPPORTED;
-  int64_t T = 0;
-  int st = check_cu(cu_seqlens_host, batch, &T);
-  if (st) return st;
-  const int64_t E = entries_of(cu_seqlens_host, batch, m);
-  Range out_r, scale_r;
-  if ((st = check_output(out_dtype, out, out_scale, E, c, &out_r, &scale_r))) return st;
-  if (E == 0) return SEQCOMP_OK;
-  if (!H || !Wt || !Ba || (csa && !Bb) || !cu_seqlens_dev) return SEQCOMP_E_NULL;
-  if (!aligned16(H) || !aligned16(Wt) || !aligned16(Ba) || (csa && !aligned16(Bb)) || !aligned16(cu_seqlens_dev))
-    return SEQCOMP_E_ALIGN;
-  const WsLayout L = ws_layout(SEQCOMP_OP_FUSED, mode, m, c, cu_seqlens_host, batch, out_dtype);
-  Range ws_r;
-  if ((st = check_workspace(workspace, workspace_bytes, L.total, &ws_r))) return st;
-  const int es = elt_size(in_dtype);
-  const int S = csa ? 4 : 2;
-  Range reads[5];
-  int nr = 0;
-  reads[nr++] = range_of(H, (size_t)T * d * es);
-  reads[nr++] = range_of(Wt, (size_t)S * c * d * es);
-  reads[nr++] = range_of(Ba, (size_t)m * c * 4);
-  if (csa) reads[nr++] = range_of(Bb, (size_t)m * c * 4);
-  reads[nr++] = range_of(cu_seqlens_dev, (size_t)(batch + 1) * 8);
-  const Range writes[3] = {out_r, scale_r, ws_r};
-  if ((st = check_alias(writes, 3, reads, nr))) return st;
+  return fused_impl(mode, m, H, d, in_dtype, Wt, c, Ba, Bb, cu_seqlens_host, cu_seqlens_dev, batch, out, out_dtype,
+                    out_scale, workspace, workspace_bytes, false, stream);
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* wsb = static_cast<char*>(workspace);
-  TileRec* tiles = reinterpret_cast<TileRec*>(wsb + L.tiles_off);
-  float* halo = csa ? reinterpret_cast<float*>(wsb + L.halo_off) : nullptr;
-  const bool fp8 = out_dtype == SEQCOMP_FP8_E4M3;
-  void* dst = fp8 ? (void*)(wsb + L.stage_off) : out;
-  const int dst_dt = fp8 ? DT_F32 : out_dtype;
-  hipError_t e = launch_plan(cu_seqlens_dev, (int)batch, (int)m, kFusedTileRows, tiles, (int)L.n_tiles, s);
-  if (e == hipSuccess)
-    e = launch_fused(mode, in_dtype, dst_dt, H, (int)d, Wt, (int)c, Ba, Bb, tiles, (int)L.n_tiles, dst, halo, s);
-  if (e == hipSuccess && csa) e = launch_csa_fixup(dst_dt, tiles, (int)L.n_tiles, (int)c, halo, dst, s);
-  if (e == hipSuccess && fp8)
-    e = launch_quant_fp8(reinterpret_cast<const float*>(dst), E, (int)c, static_cast<uint8_t*>(out), out_scale, s);
-  return hip_status(e);
+int seqcomp_compress_fused_noalloc(int mode, int64_t m, const void* H, int64_t d, int in_dtype, const void* Wt,
+                                   int64_t c, const float* Ba, const float* Bb, const int64_t* cu_seqlens_host,
+                                   const int64_t* cu_seqlens_dev, int64_t batch, void* out, int out_dtype,
+                                   float* out_scale, void* stream) {
+  return fused_impl(mode, m, H, d, in_dtype, Wt, c, Ba, Bb, cu_seqlens_host, cu_seqlens_dev, batch, out, out_dtype,
+                    out_scale, nullptr, 0, true, stream);
 }
 
 // Split-K partial products (small batches), then the fp32 staging of an fp8 output.
