@@ -200,9 +200,15 @@ def csa_full_leg(sc, synth, torch, steps, cpu: bool):
         sc.pool_csa(Y[:, :c], Y[:, c:2 * c], Y[:, 2 * c:3 * c], Y[:, 3 * c:], b["Ba"], b["Bb"], m, case.cu_seqlens,
                     "bf16")
     unfused = [lambda H=H: unfused_call(H) for H in Hs]
+    # yardstick: torch.mm (hipBLASLt) on the same product, weights as a
+    # contiguous [d x 4c] matrix, output to a preallocated buffer
+    Wdn = case.Wt_cat.t().contiguous()
+    Yr = torch.empty((T, 4 * c), dtype=torch.bfloat16, device=dev)
+    blas = [lambda H=H: torch.mm(H, Wdn, out=Yr) for H in Hs]
     med, mn, mean = _time_calls(torch, fused, steps)
     pmed, pmn, _ = _time_calls(torch, proj, steps)
     umed, umn, _ = _time_calls(torch, unfused, steps)
+    bmed, bmn, _ = _time_calls(torch, blas, steps)
     flops = 2.0 * T * d * 4 * c
     E = T // m
     res = {"workload": f"csa_full: one sequence, n={T}, d={d}, c={c}, m={m} -> {E} entries, bf16 in/out "
@@ -215,7 +221,9 @@ def csa_full_leg(sc, synth, torch, steps, cpu: bool):
                                                         "project_csa_full")},
            "unfused": {"ms_median": umed, "ms_min": umn, "entries_per_s": E / (umed * 1e-3),
                        "fused_speedup": umed / med,
-                       "path": "seqcomp_project to bf16 [T x 4c], then seqcomp_pool_csa on its column slices"}}
+                       "path": "seqcomp_project to bf16 [T x 4c], then seqcomp_pool_csa on its column slices"},
+           "hipblaslt_mm": {"ms_median": bmed, "ms_min": bmn,
+                            "roofline": _mfma_roofline(flops, bmed, "torch.mm (hipBLASLt), the same product")}}
     if cpu:
         import oracle
         ne = 256                                            # first 256 entries: 1024 tokens
@@ -225,7 +233,7 @@ def csa_full_leg(sc, synth, torch, steps, cpu: bool):
         run = lambda: oracle.csa_compress_sequence(H, W["W_KVa"], W["W_KVb"], W["W_Za"], W["W_Zb"], bb["Ba"],
                                                    bb["Bb"], m)
         res["cpu_oracle"] = _oracle_legs(run, ne, ne * m, f"first {ne} entries ({ne * m} tokens)")
-    del case, Hs, Y
+    del case, Hs, Y, Yr, Wdn
     torch.cuda.empty_cache()
     return res
 
@@ -247,9 +255,13 @@ def hca_full_leg(sc, synth, torch, steps, cpu: bool):
     def unfused():
         proj()
         sc.pool_hca(Y[:, :c], Y[:, c:], B, m, case.cu_seqlens, "bf16")
+    Wdn = case.Wt_cat.t().contiguous()
+    Yr = torch.empty((T, 2 * c), dtype=torch.bfloat16, device=dev)
+    blas = lambda: torch.mm(case.H, Wdn, out=Yr)
     med, mn, _ = _time_calls(torch, fused, steps)
     pmed, pmn, _ = _time_calls(torch, proj, steps)
     umed, umn, _ = _time_calls(torch, unfused, steps)
+    bmed, bmn, _ = _time_calls(torch, blas, steps)
     flops = 2.0 * T * d * 2 * c
     E = T // m
     res = {"workload": f"hca_full: one sequence, n={T}, d={d}, c={c}, m'={m} -> {E} entries, bf16 in/out",
@@ -260,7 +272,9 @@ def hca_full_leg(sc, synth, torch, steps, cpu: bool):
                                                         "project_hca_full")},
            "unfused": {"ms_median": umed, "ms_min": umn, "entries_per_s": E / (umed * 1e-3),
                        "fused_speedup": umed / med,
-                       "path": "seqcomp_project to bf16 [T x 2c], then seqcomp_pool_hca on its column slices"}}
+                       "path": "seqcomp_project to bf16 [T x 2c], then seqcomp_pool_hca on its column slices"},
+           "hipblaslt_mm": {"ms_median": bmed, "ms_min": bmn,
+                            "roofline": _mfma_roofline(flops, bmed, "torch.mm (hipBLASLt), the same product")}}
     if cpu:
         import oracle
         ne = 16                                             # first 16 entries: 2048 tokens
@@ -269,7 +283,7 @@ def hca_full_leg(sc, synth, torch, steps, cpu: bool):
         Bh = _f64(torch, B)
         run = lambda: oracle.hca_compress_sequence(H, W["W_KV"], W["W_Z"], Bh, m)
         res["cpu_oracle"] = _oracle_legs(run, ne, ne * m, f"first {ne} entries ({ne * m} tokens)")
-    del case, Y
+    del case, Y, Yr, Wdn
     torch.cuda.empty_cache()
     return res
 

@@ -82,7 +82,7 @@ struct WsLayout {
 WsLayout ws_layout(int op, int mode, int64_t m, int64_t c, const int64_t* cu, int64_t batch, int out_dtype) {
   WsLayout w;
   int64_t tile_rows;
-  if (op == SEQCOMP_OP_POOL_CSA) tile_rows = pool_csa_tile_rows((int)m);
+  if (op == SEQCOMP_OP_POOL_CSA) tile_rows = pool_csa_tile_rows((int)m, c);
   else if (op == SEQCOMP_OP_POOL_HCA) tile_rows = pool_hca_tile_rows((int)m);
   else tile_rows = kFusedTileRows;
   w.n_tiles = count_tiles(cu, batch, m, tile_rows);
@@ -145,7 +145,7 @@ int run_pool(bool csa, const void* const* streams, int64_t ld_in, int in_dtype, 
   char* wsb = static_cast<char*>(ws);
   TileRec* tiles = reinterpret_cast<TileRec*>(wsb + L.tiles_off);
   const int op = csa ? SEQCOMP_OP_POOL_CSA : SEQCOMP_OP_POOL_HCA;
-  const int tile_rows = op == SEQCOMP_OP_POOL_CSA ? pool_csa_tile_rows((int)m) : pool_hca_tile_rows((int)m);
+  const int tile_rows = op == SEQCOMP_OP_POOL_CSA ? pool_csa_tile_rows((int)m, c) : pool_hca_tile_rows((int)m);
   hipError_t e = launch_plan(cu_dev, (int)batch, (int)m, tile_rows, tiles, (int)L.n_tiles, st);
   if (e != hipSuccess) return hip_status(e);
   const bool fp8 = out_dtype == SEQCOMP_FP8_E4M3;

@@ -865,23 +865,10 @@ int append_splits(int64_t nb, int c) {
   return S < kAppendMaxSplits ? (int)S : kAppendMaxSplits;
 }
 
-// Compute units of the current device (one workgroup of the tile kernels fits per CU).
-int cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
 template <int DIN, int MODE, int DOUT>
 hipError_t launch_tile(const Args& a, hipStream_t stream) {
   const int G = a.n_mt * a.n_nt;
-  const int P = min(G, cu_count());
+  const int P = min(G, device_cu_count());   // one workgroup of the tile kernels fits per CU
   hipLaunchKernelGGL((tile_kernel<DIN, MODE, DOUT>), dim3(P), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }

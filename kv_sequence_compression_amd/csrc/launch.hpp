@@ -9,15 +9,19 @@
 
 namespace seqcomp {
 
-// Rows per tile of the pooling kernels: CSA (m <= 16) takes as many whole
-// blocks as fit in 256 rows; HCA (m <= 256) takes whole blocks of about 1024
-// rows, a multiple of 4 blocks (the 4 waves of a workgroup share them and the
-// bias slice staged once for all of them).
-inline int pool_csa_tile_rows(int m) { return m * (256 / m); }
+// Rows per tile of the CSA pooling kernel: 4 waves x epw entries of m rows,
+// epw = 512 / min(c, 512) entries per wave (64 lanes x 8 channels).
+inline int pool_csa_tile_rows(int m, int64_t c) { return 4 * (512 / (int)(c < 512 ? c : 512)) * m; }
+// Rows per tile of the HCA pooling kernel (m <= 256): whole blocks of about
+// 1024 rows, a multiple of 4 blocks (the 4 waves of a workgroup share them
+// and the bias slice staged once for all of them).
 inline int pool_hca_tile_rows(int m) { return m * 4 * ((1024 / m + 3) / 4); }
 constexpr int kPoolCsaMaxM = 16;
 constexpr int kPoolHcaMaxM = 256;
 constexpr int kFusedTileRows = 256;   // MFMA macro-tile height (tokens)
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
 
 // Host mirror of the device planner: number of tiles of a packed batch.
 int64_t count_tiles(const int64_t* cu, int64_t batch, int64_t m, int64_t tile_rows);

@@ -1,7 +1,9 @@
-// Tile planner: splits every sequence of a packed batch into tiles of at most
+// Tile planner (one or more workgroups): splits every sequence of a packed batch into tiles of at most
 // `tile_rows` rows made of complete blocks of m rows (a sequence of L tokens
 // has floor(L/m) entries; the tail block is dropped), and records where each
 // tile's entries go in the packed output.
+#include <algorithm>
+
 #include "launch.hpp"
 
 namespace seqcomp {
@@ -50,9 +52,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_tiles_kernel(const int64_t*
     const int chunk_tiles = s_tile_end[kPlanThreads - 1];
     const int base_tile = s_base_tile, base_ent = s_base_ent;
     // Cooperative write: tile k of this chunk belongs to the first sequence
-    // whose inclusive tile prefix exceeds k.
+    // whose inclusive tile prefix exceeds k.  Every workgroup runs the same
+    // scan; workgroup g writes the g-th of gridDim.x equal ranges of the
+    // chunk's tiles.
     const int n_seq = min(kPlanThreads, batch - b0);      // sequences of this chunk
-    for (int k = tid; k < chunk_tiles; k += kPlanThreads) {
+    const int per_wg = (chunk_tiles + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int k_lo = (int)blockIdx.x * per_wg, k_hi = min(chunk_tiles, k_lo + per_wg);
+    for (int k = k_lo + tid; k < k_hi; k += kPlanThreads) {
       int lo = 0, hi = n_seq - 1;
       while (lo < hi) {
         const int mid = (lo + hi) >> 1;
@@ -80,6 +86,18 @@ __global__ __launch_bounds__(kPlanThreads) void plan_tiles_kernel(const int64_t*
 
 }  // namespace
 
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 int64_t count_tiles(const int64_t* cu, int64_t batch, int64_t m, int64_t tile_rows) {
   int64_t n = 0;
   for (int64_t b = 0; b < batch; ++b) {
@@ -91,7 +109,10 @@ int64_t count_tiles(const int64_t* cu, int64_t batch, int64_t m, int64_t tile_ro
 
 hipError_t launch_plan(const int64_t* cu_dev, int batch, int m, int tile_rows, TileRec* tiles, int n_tiles,
                        hipStream_t stream) {
-  hipLaunchKernelGGL(plan_tiles_kernel, dim3(1), dim3(kPlanThreads), 0, stream, cu_dev, batch, m, tile_rows,
+  // one workgroup per 1024 tile records (at most 128): a single workgroup took
+  // 40-55 us to write the 65536 records of the long-context CSA pooling call
+  const int wgs = std::max(1, std::min(128, (n_tiles + 1023) / 1024));
+  hipLaunchKernelGGL(plan_tiles_kernel, dim3(wgs), dim3(kPlanThreads), 0, stream, cu_dev, batch, m, tile_rows,
                      tiles, n_tiles);
   return hipGetLastError();
 }

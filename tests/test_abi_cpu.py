@@ -66,9 +66,12 @@ def test_num_entries_and_workspace(lib):
     # bf16 output: tile table only; fp8 adds fp32 staging; fused CSA adds halo triples
     one = _cu(0, 8192)
     tiles = 8192 // 256
-    assert lib.seqcomp_workspace_bytes(_lib.OP_POOL_CSA, 0, 4, 512, _p(one), 1, _lib.BF16) == 512
+    # CSA pooling: tiles of 4 entries (one per wave) at c = 512 -> 512 tiles of 16 rows
+    assert lib.seqcomp_workspace_bytes(_lib.OP_POOL_CSA, 0, 4, 512, _p(one), 1, _lib.BF16) == 512 * 16
     assert lib.seqcomp_workspace_bytes(_lib.OP_POOL_HCA, 0, 128, 512, _p(one), 1, _lib.BF16) == 256   # 16 tiles of 4 entries
-    assert lib.seqcomp_workspace_bytes(_lib.OP_POOL_CSA, 0, 4, 512, _p(one), 1, _lib.FP8_E4M3) == 512 + 2048 * 512 * 4
+    assert lib.seqcomp_workspace_bytes(_lib.OP_POOL_CSA, 0, 4, 512, _p(one), 1, _lib.FP8_E4M3) == 512 * 16 + 2048 * 512 * 4
+    # narrower channels: 512 / c entries per wave (c = 128: 16 entries, 64 rows per tile)
+    assert lib.seqcomp_workspace_bytes(_lib.OP_POOL_CSA, 0, 4, 128, _p(one), 1, _lib.BF16) == (8192 // 64) * 16
     assert lib.seqcomp_workspace_bytes(_lib.OP_FUSED, 0, 4, 512, _p(one), 1, _lib.BF16) == 512 + tiles * 6 * 512 * 4
     assert lib.seqcomp_workspace_bytes(_lib.OP_FUSED, 1, 128, 512, _p(_cu(0, 100)), 1, _lib.BF16) == 0
     assert lib.seqcomp_workspace_bytes(7, 0, 4, 512, _p(one), 1, _lib.BF16) == ctypes.c_size_t(-1).value

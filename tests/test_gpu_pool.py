@@ -155,7 +155,7 @@ def test_pool_long_context_full_size_sampled(gpu_device):
     out, _ = sc.pool_csa(st["Ca"], st["Cb"], st["Za"], st["Zb"], b["Ba"], b["Bb"], 4, cu, "bf16")
     outh, _ = sc.pool_hca(st["Ca"], st["Za"], b["B"], 128, cu, "bf16")
     assert out.shape == (262144, c) and outh.shape == (8192, c)
-    idx = sample_entries(262144, 48, seed=5, must=(0, 1, 63, 64, 262143))
+    idx = sample_entries(262144, 256, seed=5, must=(0, 1, 3, 4, 63, 64, 2047, 2048, 262143))
     Ba, Bb = to64(b["Ba"]), to64(b["Bb"])
     got = to64(out[torch.from_numpy(idx).to(gpu_device)])
     for k, i in enumerate(idx):
