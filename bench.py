@@ -479,6 +479,33 @@ LEGS = ("step", "csa_full", "hca_full", "pool", "indexer_keys", "decode_append",
         "hca_attention")
 
 
+def pool_ceiling(torch, st, n, steps, bytes_csa, csa_ms):
+    """The CSA pooling call's memory traffic with no arithmetic (the
+    measurement-only stream_mix probe): the same rows read in the same order
+    with non-temporal loads, with and without the 1 KiB output row per entry.
+    The read+write rate is the ceiling the pooling call is held against."""
+    import ctypes
+    path = os.path.join(ROOT, "kv_sequence_compression_amd", "libseqcomp_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    fn = lib.seqcomp_probe_stream_mix
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    dst = torch.empty((n // 4, 512), dtype=torch.bfloat16, device=st["Ca"].device)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ptrs = [ctypes.c_void_p(st[k].data_ptr()) for k in ("Ca", "Cb", "Za", "Zb")]
+    res = {}
+    for name, write, nbytes in (("read_only", 0, 4 * n * 1024), ("read_write", 1, bytes_csa)):
+        call = lambda: fn(*ptrs, n // 4, ctypes.c_void_p(dst.data_ptr()), write, stream)
+        _, _, mean = _time_calls(torch, call, steps)
+        res[name] = {"ms": mean, "tbs": nbytes / (mean * 1e-3) / 1e12}
+    res["pool_csa_over_read_write"] = res["read_write"]["ms"] / csa_ms
+    res["probe"] = "kv_sequence_compression_amd/probe/stream_mix.hip"
+    del dst
+    return res
+
+
 def tiny_cpu_oracle(synth, torch):
     """The oracle on the whole tiny CSA workload (n = 64, d = 64, c = 32,
     m = 4), repeated for a measurable time."""
@@ -654,6 +681,7 @@ def main():
                              "kernel": "HCA pooling call", "algorithmic_bytes_per_launch": bytes_hca},
             "hca_roofline_frac": gbs_hca / PEAK_HBM_GBS,
         }
+        out["pool_only"]["ceiling"] = pool_ceiling(torch, st, n, args.pool_steps, bytes_csa, pcsa)
         if cpu:
             out["pool_only"]["cpu_oracle"] = pool_cpu_oracle(torch, pc)
         del pc, st
@@ -663,7 +691,7 @@ def main():
         out["indexer_keys"] = indexer_keys(sc, synth, torch, csa, lengths, args.steps)
         _progress("indexer-key compressor measured")
     if "decode_append" in legs:
-        out["decode_append"] = decode_append(sc, torch, csa, (64, 1024, 4096), args.steps)
+        out["decode_append"] = decode_append(sc, torch, csa, (1, 64, 256, 512, 1024, 4096), args.steps)
         _progress("decode append measured")
     if "rope_store" in legs:
         out["rope_store"] = rope_store(sc, torch, csa, args.steps)

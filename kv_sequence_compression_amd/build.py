@@ -2,7 +2,8 @@
 
 Usage: python -m kv_sequence_compression_amd.build [-v]
 Produces kv_sequence_compression_amd/libseqcomp.so from csrc/*.hip and
-csrc/abi.cpp; objects go to kv_sequence_compression_amd/_build/.
+csrc/abi.cpp (objects go to kv_sequence_compression_amd/_build/), and the
+measurement-only libseqcomp_probe.so from probe/stream_mix.hip.
 """
 
 from __future__ import annotations
@@ -19,6 +20,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libseqcomp.so")
+# measurement-only module for bench.py (the pooling call's traffic, no arithmetic)
+PROBE_SRC = os.path.join(PKG, "probe", "stream_mix.hip")
+PROBE_LIB = os.path.join(PKG, "libseqcomp_probe.so")
 ARCH = "gfx950"
 
 COMMON = [
@@ -75,6 +79,9 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *[j[1] for j in jobs]])
     os.replace(tmp, LIB)
+    ptmp = PROBE_LIB + ".tmp"
+    run([hipcc, *COMMON, "-shared", "-o", ptmp, PROBE_SRC])
+    os.replace(ptmp, PROBE_LIB)
     return LIB
 
 

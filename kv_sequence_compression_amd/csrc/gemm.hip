@@ -741,16 +741,14 @@ __global__ __launch_bounds__(256) void csa_fixup_kernel(const TileRec* __restric
   }
 }
 
-// Split-K form of the CSA append, for batches too small to fill the chip with
-// 256 x 256 tiles (64 blocks are one row of 8 tiles, each of which would walk
-// all of K on one CU).  Workgroup (L, s) multiplies K slabs
+// Split-K form of the big-tile CSA append, for mid-size batches whose
+// 256 x 256 tiles fill a quarter to all but one of 256 workgroups (1024
+// blocks are 16 x 8 tiles).  Workgroup (L, s) multiplies K slabs
 // [s nk / S, (s + 1) nk / S) of logical tile L and stores its accumulators as
 // they sit in registers; append_reduce_kernel adds the S partials of one
 // wave's 32-row M subtile and runs the append epilogue on the sum.  Partial
 // layout, in float4: [L][s][wave][ms][N subtile][element quad][lane], so
 // every store and load is one coalesced 1 KiB row.
-constexpr int kAppendMaxSplits = 16;
-constexpr int kAppendSplitTarget = 256;        // workgroups to aim for: one per CU of an MI355X
 constexpr int kPartialQuads = 4 * 4 * 64;      // float4 per (L, s, wave, ms) block: 16 KiB
 
 __device__ __forceinline__ int64_t partial_base(int64_t L, int S, int s, int w, int ms) {
@@ -856,13 +854,320 @@ __global__ __launch_bounds__(64) void append_reduce_kernel(Args a, int S, const 
   }
 }
 
-// Splits of the append's K loop for a batch of nb blocks and c channels (1:
-// no split).
-int append_splits(int64_t nb, int c) {
-  const int64_t G = ((4 * nb + kTile - 1) / kTile) * ((c + 63) / 64);
-  if (G <= 0 || G * 2 > kAppendSplitTarget) return 1;
-  const int64_t S = kAppendSplitTarget / G;
-  return S < kAppendMaxSplits ? (int)S : kAppendMaxSplits;
+// Decode append for batches too small to fill the chip with 256 x 256 tiles.
+// A narrower tile of 128 rows (32 blocks) x 128 columns (32 channels x the 4
+// streams C^a | C^b | Z^a | Z^b) is split over K when even those tiles are
+// too few.  The fp32 partial products of a call take 4 bytes x tile area x
+// splits per tile, and the splits that fill 256 workgroups fall as the tile
+// grows, so the bytes grow with the tile area: 16 MiB at 64 blocks with
+// these tiles against 32 MiB (at half the workgroups) with 256 x 256 ones.
+// Eight waves, two per SIMD: wave w holds rows [32 (w % 4), 32 (w % 4) + 32)
+// of the tile and all four streams of the tile's 32 channels (one 32 x 32
+// accumulator per stream, so its lanes see whole blocks of every stream, the
+// layout of the fused epilogue), over the even (w < 4) or odd (w >= 4)
+// k-steps of every slab; the odd half is added to the even one through LDS
+// at the end.  With two waves per SIMD each hides the other's LDS and
+// barrier waits, which a slab of only 512 MFMA cycles per SIMD exposes.  K
+// advances in the 128-byte slabs of the big kernel, copied global -> LDS
+// through a 4-stage ring three slabs ahead.
+constexpr int kSkThreads = 512;
+constexpr int kSkTile = 128;                           // tile rows and columns
+constexpr int kSkSlab = kSkTile * kRowBytes;           // 16 KiB: one operand's slab
+constexpr int kSkStages = 4;
+constexpr int kSkLdsBytes = kSkStages * 2 * kSkSlab;   // 128 KiB
+constexpr int kSkLoads = kSkTile / 8 / 8;              // copies per wave and operand slab (8 rows each): 2
+constexpr int kAppendMaxSplits = 32;
+constexpr int kAppendWorkgroups = 256;                 // workgroups to aim for: one per CU of an MI355X
+constexpr int kSkPartialQuads = 4 * 4 * 64;            // float4 per (tile, split, row block): 16 KiB
+
+// Tiles of the two append forms.
+__host__ __device__ inline int64_t big_append_tiles(int64_t nb, int c) {
+  return ((4 * nb + kTile - 1) / kTile) * ((c + 63) / 64);
+}
+__host__ __device__ inline int64_t skinny_append_tiles(int64_t nb, int c) {
+  return ((4 * nb + kSkTile - 1) / kSkTile) * ((c + 31) / 32);
+}
+
+template <int DIN>
+__device__ __forceinline__ void sk_mma(const f32x4_t& a, const f32x4_t& b, f32x16_t& acc) {
+  if (DIN == DT_BF16) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                  acc, 0, 0, 0);
+  } else {
+    // chunk 2 s + h holds fp32 k = 8 s + 4 h + t; the same permutation of k on
+    // both operands leaves the dot products unchanged
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t], b[t], acc, 0, 0, 0);
+  }
+}
+
+// Copy K slab `slab` of both operands into ring stage `stage`: wave w fills
+// rows [16 w, 16 w + 16) of each with 2 copies of 8 rows (1 KiB).
+__device__ __forceinline__ void sk_copy(__amdgpu_buffer_rsrc_t a_src, __amdgpu_buffer_rsrc_t b_src,
+                                        const uint32_t (&a_off)[kSkLoads], const uint32_t (&b_off)[kSkLoads],
+                                        char* lds, int stage, int slab, int w) {
+  char* as = lds + stage * 2 * kSkSlab;
+  char* bs = as + kSkSlab;
+  const uint32_t k = (uint32_t)slab * kRowBytes;
+#pragma unroll
+  for (int i = 0; i < kSkLoads; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(a_src, (lds_void_t*)(as + (w * kSkLoads + i) * 1024), 16, a_off[i], k,
+                                             0, 2);
+#pragma unroll
+  for (int i = 0; i < kSkLoads; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(b_src, (lds_void_t*)(bs + (w * kSkLoads + i) * 1024), 16, b_off[i], k,
+                                             0, 0);
+}
+
+// K slabs [k0, k1) of tile (mt, nt): wave w adds its k-steps (parity w / 4)
+// of row block w % 4 into acc[stream].  Ends with every wave past its last
+// LDS read and a barrier, so the caller may reuse the LDS.
+template <int DIN>
+__device__ __forceinline__ void sk_mainloop(const Args& a, int mt, int nt, int k0, int k1, char* lds, int w, int lane,
+                                            f32x16_t (&acc)[4]) {
+  const int64_t row0 = (int64_t)mt * kSkTile;
+  const int nvalid = (int)min<int64_t>(kSkTile, a.T - row0);
+  uint32_t a_off[kSkLoads], b_off[kSkLoads];
+#pragma unroll
+  for (int i = 0; i < kSkLoads; ++i) {
+    const int r = w * 16 + i * 8 + (lane >> 3);
+    const int kc = (lane & 7) ^ swz_f(r);
+    a_off[i] = (uint32_t)(min(r, nvalid - 1) * a.lda + kc * 16);
+    const int s = r >> 5, ch = min(nt * 32 + (r & 31), a.c - 1);
+    b_off[i] = (uint32_t)((int64_t)(s * a.c + ch) * a.lda + kc * 16);
+  }
+  const __amdgpu_buffer_rsrc_t a_src = raw_rsrc(a.H + row0 * a.lda + (int64_t)k0 * kRowBytes);
+  const __amdgpu_buffer_rsrc_t b_src = raw_rsrc(a.Wt + (int64_t)k0 * kRowBytes);
+  // fragment offsets as in the big kernel: subtile i's rows have swizzle
+  // x0 ^ 4 (i & 1), so chunk 2 s + h of row (lane % 32) sits at ro[s ^ 2 (i & 1)]
+  int ro[4];
+  {
+    const int h = lane >> 5;
+    const int x0 = (lane & 7) ^ ((lane >> 3) & 3);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) ro[k] = (lane & 31) * kRowBytes + ((16 * (h ^ x0)) ^ (32 * k));
+  }
+  const int rb = w & 3, kh = w >> 2;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f32x16_t{};
+  const int nks = k1 - k0;
+  for (int p = 0; p < min(3, nks); ++p) sk_copy(a_src, b_src, a_off, b_off, lds, p, p, w);
+  for (int j = 0; j < nks; ++j) {
+    const int ahead = min(2, nks - 1 - j);            // slabs issued after slab j
+    if (ahead == 2) wait_vmcnt<2 * 2 * kSkLoads>();
+    else if (ahead == 1) wait_vmcnt<2 * kSkLoads>();
+    else wait_vmcnt<0>();
+    lds_barrier();                                    // slab j in LDS; every wave is done with slab j - 1
+    if (j + 3 < nks) sk_copy(a_src, b_src, a_off, b_off, lds, (j + 3) & 3, j + 3, w);
+    const char* as = lds + (j & 3) * 2 * kSkSlab + (rb * 32) * kRowBytes;
+    const char* bs = lds + (j & 3) * 2 * kSkSlab + kSkSlab;
+    f32x4_t fa[2], fb[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int s = 2 * t + kh;
+      fa[t] = *reinterpret_cast<const f32x4_t*>(as + ro[s ^ (2 * (rb & 1))]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        fb[t][q] = *reinterpret_cast<const f32x4_t*>(bs + (q * 32) * kRowBytes + ro[s ^ (2 * (q & 1))]);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sk_mma<DIN>(fa[t], fb[t][q], acc[q]);
+  }
+  wait_lgkmcnt0();
+  lds_barrier();                                      // the ring's LDS is free
+}
+
+// Adds the odd-k-step half (waves 4..7) into the even half (waves 0..3)
+// through LDS, in the same order on every call.  Returns true in the waves
+// that hold the sum.
+__device__ __forceinline__ bool sk_combine(f32x16_t (&acc)[4], char* lds, int w, int lane) {
+  float4* x = reinterpret_cast<float4*>(lds) + (w & 3) * kSkPartialQuads + lane;
+  if (w >= 4) {
+#pragma unroll
+    for (int jn = 0; jn < 4; ++jn)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = acc[jn][4 * q4 + e];
+          asm volatile("" : "+v"(v[e]));
+        }
+        x[(jn * 4 + q4) * 64] = make_float4(v[0], v[1], v[2], v[3]);
+      }
+  }
+  __syncthreads();
+  if (w >= 4) return false;
+#pragma unroll
+  for (int jn = 0; jn < 4; ++jn)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 o = x[(jn * 4 + q4) * 64];
+      acc[jn][4 * q4 + 0] += o.x;
+      acc[jn][4 * q4 + 1] += o.y;
+      acc[jn][4 * q4 + 2] += o.z;
+      acc[jn][4 * q4 + 3] += o.w;
+    }
+  return true;
+}
+
+// Append epilogue of row block rb of a skinny tile: its run q of lane half h
+// is block 32 mt + 8 rb + 2 q + h.
+template <int DOUT>
+__device__ __forceinline__ void sk_epilogue(const Args& a, const f32x16_t (&acc)[4], int mt, int nt, int rb, int lane) {
+  const int col = lane & 31, h = lane >> 5;
+  const int ch = nt * 32 + col;
+  const bool ok = ch < a.c;
+  const int chc = min(ch, a.c - 1);
+  float ba[4], bb[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    ba[r] = a.Ba[r * a.c + chc] * kLog2e;
+    bb[r] = a.Bb[r * a.c + chc] * kLog2e;
+  }
+  const int64_t j0 = (int64_t)mt * 32 + rb * 8 + h;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t j = j0 + 2 * q;
+    const float* st = a.state_in + min(j, a.nb - 1) * 3 * a.c + chc;
+    const SoftAcc prev{st[0], st[a.c], st[2 * a.c]};
+    const SoftAcc pa = partial4(acc[2], acc[0], q, ba);
+    const SoftAcc pb = partial4(acc[3], acc[1], q, bb);
+    append_store<DOUT>(a, pa, pb, prev, j, ok, ch);
+  }
+}
+
+// Workgroup (tile L, split sp): K slabs [sp nk / S, (sp + 1) nk / S).  With
+// S = 1 it finishes the entries itself; otherwise it stores its accumulators
+// as they sit in registers ([L][sp][row block][stream][element quad][lane]
+// float4: every store one coalesced 1 KiB row) for
+// append_skinny_reduce_kernel.
+template <int DIN, int DOUT>
+__global__ __launch_bounds__(kSkThreads, 1) void append_skinny_kernel(Args a, int S, float4* __restrict__ partial) {
+  __shared__ __attribute__((aligned(1024))) char lds[kSkLdsBytes];
+  const int L = blockIdx.x / S, sp = blockIdx.x - L * S;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int mt = L / a.n_nt, nt = L - mt * a.n_nt;
+  const int k0 = (int)((int64_t)sp * a.nk / S), k1 = (int)((int64_t)(sp + 1) * a.nk / S);   // S <= nk: k1 > k0
+  f32x16_t acc[4];
+  sk_mainloop<DIN>(a, mt, nt, k0, k1, lds, w, lane, acc);
+  if (!sk_combine(acc, lds, w, lane)) return;
+  if (S == 1) {
+    sk_epilogue<DOUT>(a, acc, mt, nt, w, lane);
+    return;
+  }
+  float4* dst = partial + (((int64_t)L * S + sp) * 4 + w) * kSkPartialQuads + lane;
+#pragma unroll
+  for (int jn = 0; jn < 4; ++jn)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      // each element through a VGPR: a store fed straight from an
+      // accumulator register has been miscompiled (see epilogue_project)
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = acc[jn][4 * q4 + e];
+        asm volatile("" : "+v"(v[e]));
+      }
+      dst[(jn * 4 + q4) * 64] = make_float4(v[0], v[1], v[2], v[3]);
+    }
+}
+
+// Workgroup = (tile L, row block w) of the split form, eight waves: wave u
+// adds splits u, u + 8, ... in increasing order, then the waves' sums meet in
+// a fixed tree through LDS ((4..7 into 0..3), (2, 3 into 0, 1), 1 into 0 --
+// the same sum on every call) and wave 0 runs the append epilogue.
+template <int DOUT>
+__global__ __launch_bounds__(kSkThreads) void append_skinny_reduce_kernel(Args a, int S,
+                                                                          const float4* __restrict__ partial) {
+  __shared__ float4 xch[4][16][64];                  // 64 KiB
+  const int L = blockIdx.x >> 2, w = blockIdx.x & 3;
+  const int u = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int mt = L / a.n_nt, nt = L - mt * a.n_nt;
+  float4 sum[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) sum[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int sp = u; sp < S; sp += 8) {
+    const float4* src = partial + (((int64_t)L * S + sp) * 4 + w) * kSkPartialQuads + lane;
+    float4 v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v[k] = src[k * 64];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      sum[k].x += v[k].x; sum[k].y += v[k].y; sum[k].z += v[k].z; sum[k].w += v[k].w;
+    }
+  }
+#pragma unroll
+  for (int half = 4; half >= 1; half >>= 1) {
+    if (u >= half && u < 2 * half) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) xch[u - half][k][lane] = sum[k];
+    }
+    __syncthreads();
+    if (u < half) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const float4 o = xch[u][k][lane];
+        sum[k].x += o.x; sum[k].y += o.y; sum[k].z += o.z; sum[k].w += o.w;
+      }
+    }
+    __syncthreads();
+  }
+  if (u != 0) return;
+  f32x16_t acc[4];
+#pragma unroll
+  for (int jn = 0; jn < 4; ++jn)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      acc[jn][4 * q4 + 0] = sum[jn * 4 + q4].x;
+      acc[jn][4 * q4 + 1] = sum[jn * 4 + q4].y;
+      acc[jn][4 * q4 + 2] = sum[jn * 4 + q4].z;
+      acc[jn][4 * q4 + 3] = sum[jn * 4 + q4].w;
+    }
+  sk_epilogue<DOUT>(a, acc, mt, nt, w, lane);
+}
+
+// Form of a decode append of nb blocks:
+//  * BIG: the 256 x 256 tiles alone fill 256 workgroups;
+//  * BIG_SPLIT: they fill at least 64, and the K loop is split S ways so
+//    that about 256 run (measured at 1024 blocks: 101 + 19 us, against
+//    160 us for the unsplit 128 x 128 tiles, whose copies move twice the
+//    bytes per MFMA);
+//  * SKINNY: smaller batches, 128 x 128 tiles split S >= 1 ways (S = 1: no
+//    partials; measured at 64 blocks: 16 + 7.5 us, against 18.5 + 12 us for
+//    256 x 256 tiles split 16 ways).
+// S is capped at the K loop's slab count nk.  A function of nb, c and nk
+// only, so the workspace size does not depend on the device.
+enum AppendForm { APPEND_BIG = 0, APPEND_BIG_SPLIT = 1, APPEND_SKINNY = 2 };
+struct AppendPlan {
+  int form;
+  int S;
+  int64_t tiles;
+};
+
+AppendPlan append_plan(int64_t nb, int c, int nk) {
+  AppendPlan p{};
+  const int64_t gb = big_append_tiles(nb, c);
+  int64_t S;
+  if (gb >= kAppendWorkgroups) {
+    p.form = APPEND_BIG;
+    p.tiles = gb;
+    S = 1;
+  } else if (gb * 4 >= kAppendWorkgroups) {
+    p.form = APPEND_BIG_SPLIT;
+    p.tiles = gb;
+    S = kAppendWorkgroups / gb;
+  } else {
+    p.form = APPEND_SKINNY;
+    p.tiles = skinny_append_tiles(nb, c);
+    S = kAppendWorkgroups / p.tiles;
+  }
+  S = S < 1 ? 1 : S > kAppendMaxSplits ? kAppendMaxSplits : S;
+  p.S = (int)(S > nk ? nk : S);
+  return p;
 }
 
 template <int DIN, int MODE, int DOUT>
@@ -928,10 +1233,12 @@ hipError_t launch_fused(int mode, int in_dt, int out_dt, const void* H, int d, c
 }
 
 size_t append_partial_bytes(int64_t nb, int c) {
-  const int S = append_splits(nb, c);
-  if (S <= 1) return 0;
-  const int64_t G = ((4 * nb + kTile - 1) / kTile) * ((c + 63) / 64);
-  return (size_t)G * S * 4 * 4 * kPartialQuads * sizeof(float4);
+  // sized for the uncapped split count, so the size depends on nb and c
+  // only; a call whose K has fewer slabs than that uses less of it
+  const AppendPlan p = append_plan(nb, c, 1 << 30);
+  if (p.S <= 1) return 0;
+  const size_t per = p.form == APPEND_BIG_SPLIT ? (size_t)4 * 4 * kPartialQuads : (size_t)4 * kSkPartialQuads;
+  return (size_t)p.tiles * p.S * per * sizeof(float4);
 }
 
 hipError_t launch_csa_append(int in_dt, int out_dt, const void* H, int64_t nb, int d, const void* Wt, int c,
@@ -952,22 +1259,38 @@ hipError_t launch_csa_append(int in_dt, int out_dt, const void* H, int64_t nb, i
   a.state_out = state_out;
   a.nb = nb;
   a.n_out = 1;
-  a.n_mt = (int)((a.T + kTile - 1) / kTile);
-  a.n_nt = (c + 63) / 64;
-  const int S = min(append_splits(nb, c), a.nk);
-  if (S <= 1 || partial == nullptr) return dispatch<MODE_CSA_APPEND>(in_dt, out_dt, a, stream);
-  const int G = a.n_mt * a.n_nt;
+  const AppendPlan p = append_plan(nb, c, a.nk);
+  const int G = (int)p.tiles, S = p.S;
+  if (S > 1 && partial == nullptr) return hipErrorInvalidValue;
   float4* part = static_cast<float4*>(partial);
-  if (in_dt == DT_BF16)
-    hipLaunchKernelGGL(append_splitk_kernel<DT_BF16>, dim3(G * S), dim3(kThreads), 0, stream, a, S, part);
-  else
-    hipLaunchKernelGGL(append_splitk_kernel<DT_F32>, dim3(G * S), dim3(kThreads), 0, stream, a, S, part);
+  if (p.form != APPEND_SKINNY) {
+    a.n_mt = (int)((a.T + kTile - 1) / kTile);
+    a.n_nt = (c + 63) / 64;
+    if (S == 1) return dispatch<MODE_CSA_APPEND>(in_dt, out_dt, a, stream);
+    if (in_dt == DT_BF16)
+      hipLaunchKernelGGL(append_splitk_kernel<DT_BF16>, dim3(G * S), dim3(kThreads), 0, stream, a, S, part);
+    else
+      hipLaunchKernelGGL(append_splitk_kernel<DT_F32>, dim3(G * S), dim3(kThreads), 0, stream, a, S, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (out_dt == DT_BF16)
+      hipLaunchKernelGGL(append_reduce_kernel<DT_BF16>, dim3(G * 16), dim3(64), 0, stream, a, S, part);
+    else
+      hipLaunchKernelGGL(append_reduce_kernel<DT_F32>, dim3(G * 16), dim3(64), 0, stream, a, S, part);
+    return hipGetLastError();
+  }
+  a.n_mt = (int)((a.T + kSkTile - 1) / kSkTile);
+  a.n_nt = (c + 31) / 32;
+  auto split = [&](auto kern) { hipLaunchKernelGGL(kern, dim3(G * S), dim3(kSkThreads), 0, stream, a, S, part); };
+  if (in_dt == DT_BF16) out_dt == DT_BF16 ? split(append_skinny_kernel<DT_BF16, DT_BF16>)
+                                          : split(append_skinny_kernel<DT_BF16, DT_F32>);
+  else out_dt == DT_BF16 ? split(append_skinny_kernel<DT_F32, DT_BF16>) : split(append_skinny_kernel<DT_F32, DT_F32>);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || S == 1) return e;
   if (out_dt == DT_BF16)
-    hipLaunchKernelGGL(append_reduce_kernel<DT_BF16>, dim3(G * 16), dim3(64), 0, stream, a, S, part);
+    hipLaunchKernelGGL(append_skinny_reduce_kernel<DT_BF16>, dim3(G * 4), dim3(kSkThreads), 0, stream, a, S, part);
   else
-    hipLaunchKernelGGL(append_reduce_kernel<DT_F32>, dim3(G * 16), dim3(64), 0, stream, a, S, part);
+    hipLaunchKernelGGL(append_skinny_reduce_kernel<DT_F32>, dim3(G * 4), dim3(kSkThreads), 0, stream, a, S, part);
   return hipGetLastError();
 }
 

@@ -185,14 +185,20 @@ def append(lib, **kw):
 
 def test_append_workspace(lib):
     f = lib.seqcomp_append_workspace_bytes
-    part = 256 * 1024                                    # split-K partials of one workgroup
-    # 64 blocks, c = 512: 1 x 8 tiles, K split 16 ways
-    assert f(64, 512, _lib.BF16) == 8 * 16 * part
-    # 100 blocks: 2 x 8 tiles, 16 ways; fp8 adds the fp32 staging of the entries
-    assert f(100, 512, _lib.BF16) == 16 * 16 * part
-    assert f(100, 512, _lib.FP8_E4M3) == 16 * 16 * part + 100 * 512 * 4
-    # 1024 blocks: 16 x 8 = 128 tiles, split 2 ways; 4096 blocks: 512 tiles, no split
-    assert f(1024, 512, _lib.BF16) == 128 * 2 * part
+    part = 64 * 1024                                     # split-K partials of one 128 x 128 tile and split
+    # 64 blocks, c = 512: 2 x 16 tiles of 128 x 128, K split 8 ways
+    assert f(64, 512, _lib.BF16) == 32 * 8 * part
+    # 100 blocks: 4 x 16 tiles, 4 ways; fp8 adds the fp32 staging of the entries
+    assert f(100, 512, _lib.BF16) == 64 * 4 * part
+    assert f(100, 512, _lib.FP8_E4M3) == 64 * 4 * part + 100 * 512 * 4
+    # 1 block: 16 tiles, 16 ways; c = 160 (5 channel tiles): 5 tiles, capped at 32 ways
+    assert f(1, 512, _lib.BF16) == 16 * 16 * part
+    assert f(20, 160, _lib.BF16) == 5 * 32 * part
+    # 400 blocks: 7 x 8 tiles of 256 x 256 are too few, 13 x 16 = 208 of 128 x 128 run unsplit
+    assert f(400, 512, _lib.BF16) == 0
+    # 1024 blocks: 16 x 8 = 128 tiles of 256 x 256, K split 2 ways (256 KiB per tile and split);
+    # 4096 blocks: 512 tiles of 256 x 256, no split
+    assert f(1024, 512, _lib.BF16) == 128 * 2 * 256 * 1024
     assert f(4096, 512, _lib.BF16) == 0
     assert f(4096, 512, _lib.FP8_E4M3) == 4096 * 512 * 4
     assert f(0, 512, _lib.FP8_E4M3) == 0
@@ -213,7 +219,7 @@ def test_append_workspace(lib):
     (dict(st_out=0), "SEQCOMP_E_NULL"),
     (dict(out=0), "SEQCOMP_E_NULL"),
     (dict(out_dt=_lib.FP8_E4M3, scale=0, ws=WS, ws_bytes=1 << 20), "SEQCOMP_E_NULL"),
-    (dict(out_dt=_lib.FP8_E4M3, scale=SCALE, ws_bytes=16 * 16 * 256 * 1024), "SEQCOMP_E_WORKSPACE"),
+    (dict(out_dt=_lib.FP8_E4M3, scale=SCALE, ws_bytes=64 * 4 * 64 * 1024), "SEQCOMP_E_WORKSPACE"),   # no staging
     (dict(ws=0, ws_bytes=0), "SEQCOMP_E_WORKSPACE"),     # the split-K partials of a small batch
     (dict(st_in=STATE + 4), "SEQCOMP_E_ALIGN"),
     (dict(st_out=STATE + 16), "SEQCOMP_E_ALIAS"),          # partial overlap with the input state

@@ -87,8 +87,9 @@ def test_append_bf16_in_place_and_fp8(gpu_device):
 
 def test_append_split_k_full_depth(gpu_device):
     """64 sequences of two blocks at the full projection depth (d = 7168,
-    bf16, c = 512): one row of 8 tiles, so each call splits K over 16
-    workgroups per tile; both appends against the oracle."""
+    bf16, c = 512): 2 x 16 tiles of 128 x 128, so each call splits K over 8
+    workgroups per tile (14 slabs each) and a reduce kernel adds them; both
+    appends against the oracle."""
     case = synth.compressor_case("csa", [8] * 64, 7168, 512, 4, seed=6, in_dtype="bf16", bias_std=0.3,
                                  device=gpu_device)
     ref = _oracle(case)
@@ -96,10 +97,44 @@ def test_append_split_k_full_depth(gpu_device):
     assert row_rel_err(to64(out), ref).max() <= 2e-2
 
 
+def test_append_uneven_split_and_partial_channel_tile(gpu_device):
+    """20 sequences, c = 160 (5 channel tiles of 32, every one full) at
+    d = 7168: 5 tiles split 32 ways, 3 or 4 of the 112 K slabs each, then
+    fp8 output through the same partials."""
+    case = synth.compressor_case("csa", [8] * 20, 7168, 160, 4, seed=8, in_dtype="bf16", bias_std=0.3,
+                                 device=gpu_device)
+    ref = _oracle(case)
+    out, _ = _append_all(case, "bf16", in_place=False)
+    assert row_rel_err(to64(out), ref).max() <= 2e-2
+    q, s = _append_all(case, "fp8", in_place=True)
+    check_fp8(q, s, ref, 2e-2)
+
+
 def test_append_unsplit_many_tiles(gpu_device):
-    """520 single-block sequences with c = 1024 make 9 x 16 = 144 tiles, more
-    than the split-K path takes: the K loop runs whole in each tile."""
+    """520 single-block sequences with c = 1024 make 9 x 16 = 144 tiles of
+    256 x 256: the big-tile kernel runs the K loop whole in each tile."""
     case = synth.compressor_case("csa", [4] * 520, 64, 1024, 4, seed=7, in_dtype="f32", bias_std=0.3,
+                                 device=gpu_device)
+    ref = _oracle(case)
+    out, _ = _append_all(case, "f32", in_place=False)
+    assert max_abs_err(to64(out), ref) <= 2e-5
+
+
+def test_append_skinny_unsplit(gpu_device):
+    """400 single-block sequences at c = 512: 7 x 8 big tiles are too few,
+    13 x 16 = 208 tiles of 128 x 128 run unsplit and the tile kernel
+    finishes the entries itself (its odd-k-step waves added through LDS)."""
+    case = synth.compressor_case("csa", [4] * 400, 64, 512, 4, seed=10, in_dtype="f32", bias_std=0.3,
+                                 device=gpu_device)
+    ref = _oracle(case)
+    out, _ = _append_all(case, "f32", in_place=True)
+    assert max_abs_err(to64(out), ref) <= 2e-5
+
+
+def test_append_big_tile_split(gpu_device):
+    """1024 single-block sequences at c = 512: 16 x 8 = 128 big tiles, K split
+    2 ways (both K slabs of d = 64 fp32), then the big-tile reduce."""
+    case = synth.compressor_case("csa", [4] * 1024, 64, 512, 4, seed=11, in_dtype="f32", bias_std=0.3,
                                  device=gpu_device)
     ref = _oracle(case)
     out, _ = _append_all(case, "f32", in_place=False)
