@@ -54,13 +54,14 @@ def _events(torch, n):
 
 def _traffic(kernel_key: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when the summary is missing or was taken on other kernel sources."""
+    None when the summary is missing or was taken on other sources of that
+    kernel."""
     try:
         with open(TRAFFIC_FILE, encoding="utf-8") as f:
             rec = json.load(f)
-        from kv_sequence_compression_amd.build import source_digest
+        from kv_sequence_compression_amd.build import KERNEL_SOURCES, source_digest
         entry = rec["kernels"][kernel_key]
-        if entry.get("source_digest") != source_digest():
+        if entry.get("source_digest") != source_digest(KERNEL_SOURCES[entry["sources"]]):
             return None
         return float(entry["bytes_per_launch"])
     except (OSError, KeyError, ValueError, ImportError):
@@ -479,6 +480,34 @@ LEGS = ("step", "csa_full", "hca_full", "pool", "indexer_keys", "decode_append",
         "hca_attention")
 
 
+def mfma_ceiling(torch, reps: int = 3, iters: int = 57344):
+    """Sustained rate of the bf16 matrix cores with no data movement (the
+    measurement-only seqcomp_probe_mfma: 16 independent 32x32x16 MFMA chains
+    per wave on random bf16 operands in registers, one wave per SIMD, ~20 ms
+    per call): the power-limited ceiling of the instruction the tile kernels
+    use."""
+    import ctypes
+    path = os.path.join(ROOT, "kv_sequence_compression_amd", "libseqcomp_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    fn = lib.seqcomp_probe_mfma
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    data = torch.randn((cus * 256 * 128,), dtype=torch.bfloat16, device=dev)
+    sink = torch.empty((cus * 256,), dtype=torch.float32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    call = lambda: fn(ctypes.c_void_p(data.data_ptr()), iters, ctypes.c_void_p(sink.data_ptr()), stream)
+    med, mn, mean = _time_calls(torch, call, reps, warmup=1)
+    flops = float(iters) * 16 * 32768 * 4 * cus
+    tf = flops / (med * 1e-3) / 1e12
+    del data, sink
+    return {"tflops": tf, "frac": tf / PEAK_BF16_TFLOPS, "ms": med,
+            "probe": "kv_sequence_compression_amd/probe/ceilings.hip (seqcomp_probe_mfma)"}
+
+
 def pool_ceiling(torch, st, n, steps, bytes_csa, csa_ms):
     """The CSA pooling call's memory traffic with no arithmetic (the
     measurement-only stream_mix probe): the same rows read in the same order
@@ -501,7 +530,7 @@ def pool_ceiling(torch, st, n, steps, bytes_csa, csa_ms):
         _, _, mean = _time_calls(torch, call, steps)
         res[name] = {"ms": mean, "tbs": nbytes / (mean * 1e-3) / 1e12}
     res["pool_csa_over_read_write"] = res["read_write"]["ms"] / csa_ms
-    res["probe"] = "kv_sequence_compression_amd/probe/stream_mix.hip"
+    res["probe"] = "kv_sequence_compression_amd/probe/ceilings.hip (seqcomp_probe_stream_mix)"
     del dst
     return res
 
@@ -645,6 +674,16 @@ def main():
     if "hca_full" in legs:
         out["hca_full"] = hca_full_leg(sc, synth, torch, max(args.steps, 10), cpu)
         _progress("HCA workload measured")
+    if any(x in legs for x in ("step", "csa_full", "hca_full")):
+        ceil = mfma_ceiling(torch)
+        if ceil is not None:
+            out["mfma_ceiling"] = ceil
+            for key in ("roofline", "csa_full", "hca_full"):
+                r = out.get(key)
+                r = r.get("roofline", r) if isinstance(r, dict) and key != "roofline" else r
+                if isinstance(r, dict) and "achieved" in r:
+                    r["frac_of_mfma_ceiling"] = r["achieved"] / ceil["tflops"]
+            _progress("matrix-core ceiling measured")
     if "pool" in legs:
         pc = synth.pool_case(1 << 20, 512, seed=0, dtype="bf16", device=dev, bias_std=0.02)
         st, pb = pc.streams, pc.biases

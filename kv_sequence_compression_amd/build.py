@@ -3,7 +3,7 @@
 Usage: python -m kv_sequence_compression_amd.build [-v]
 Produces kv_sequence_compression_amd/libseqcomp.so from csrc/*.hip and
 csrc/abi.cpp (objects go to kv_sequence_compression_amd/_build/), and the
-measurement-only libseqcomp_probe.so from probe/stream_mix.hip.
+measurement-only libseqcomp_probe.so from probe/ceilings.hip.
 """
 
 from __future__ import annotations
@@ -20,8 +20,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libseqcomp.so")
-# measurement-only module for bench.py (the pooling call's traffic, no arithmetic)
-PROBE_SRC = os.path.join(PKG, "probe", "stream_mix.hip")
+# measurement-only module for bench.py: the pooling call's traffic with no
+# arithmetic, and the bf16 matrix cores with no data movement
+PROBE_SRC = os.path.join(PKG, "probe", "ceilings.hip")
 PROBE_LIB = os.path.join(PKG, "libseqcomp_probe.so")
 ARCH = "gfx950"
 
@@ -47,12 +48,27 @@ def sources():
     return srcs + [os.path.join(CSRC, "abi.cpp")]
 
 
-def source_digest() -> str:
-    """SHA-256 over the library sources and the public header (identifies the
-    kernels a stored profile or counter summary was taken on)."""
+# The source files each measured kernel is built from (a stored counter
+# summary is valid for a kernel while these files are unchanged).
+KERNEL_SOURCES = {
+    "gemm": ["csrc/gemm.hip", "csrc/common.hpp", "csrc/amdgcn.hpp", "csrc/launch.hpp"],
+    "pool": ["csrc/pool.hip", "csrc/common.hpp", "csrc/launch.hpp"],
+    "indexer": ["csrc/indexer.hip", "csrc/common.hpp", "csrc/amdgcn.hpp", "csrc/launch.hpp"],
+    "mqa": ["csrc/mqa.hip", "csrc/common.hpp", "csrc/amdgcn.hpp", "csrc/launch.hpp"],
+}
+
+
+def source_digest(files=None) -> str:
+    """SHA-256 over library sources (paths relative to the package; default:
+    every source and the public header).  Identifies the kernels a stored
+    profile or counter summary was taken on."""
     h = hashlib.sha256()
-    for path in sources() + sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hpp")) + [
-            os.path.join(ROOT, "include", "seqcomp.h")]:
+    if files is None:
+        paths = sources() + sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hpp")) + [
+            os.path.join(ROOT, "include", "seqcomp.h")]
+    else:
+        paths = [os.path.join(PKG, f) for f in files]
+    for path in paths:
         with open(path, "rb") as f:
             h.update(os.path.basename(path).encode() + b"\0" + f.read())
     return h.hexdigest()
