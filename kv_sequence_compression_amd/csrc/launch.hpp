@@ -12,10 +12,15 @@ namespace seqcomp {
 // Rows per tile of the CSA pooling kernel: 4 waves x epw entries of m rows,
 // epw = 512 / min(c, 512) entries per wave (64 lanes x 8 channels).
 inline int pool_csa_tile_rows(int m, int64_t c) { return 4 * (512 / (int)(c < 512 ? c : 512)) * m; }
-// Rows per tile of the HCA pooling kernel (m <= 256): whole blocks of about
-// 1024 rows, a multiple of 4 blocks (the 4 waves of a workgroup share them
-// and the bias slice staged once for all of them).
-inline int pool_hca_tile_rows(int m) { return m * 4 * ((1024 / m + 3) / 4); }
+// Rows per tile of the HCA pooling kernels.  m <= 128: the whole-row kernel,
+// 8 / ceil(m / 16) entries per tile (one workgroup of 8 waves, ceil(m / 16)
+// waves per entry); 128 < m <= 256: whole blocks of about 1024 rows, a
+// multiple of 4 blocks (the 4 waves of a workgroup share them and the bias
+// slice staged once for all of them).
+constexpr int kPoolHcaRowsMaxM = 128;
+inline int pool_hca_tile_rows(int m) {
+  return m <= kPoolHcaRowsMaxM ? (8 / ((m + 15) / 16)) * m : m * 4 * ((1024 / m + 3) / 4);
+}
 constexpr int kPoolCsaMaxM = 16;
 constexpr int kPoolHcaMaxM = 256;
 constexpr int kFusedTileRows = 256;   // MFMA macro-tile height (tokens)

@@ -142,6 +142,12 @@ __device__ __forceinline__ void fold_chunk(SoftAcc (&acc)[8], const Raw8<DIN> (&
 }
 
 template <int DOUT>
+__device__ __forceinline__ void store1_pool(char* out, int64_t idx, float v) {
+  if (DOUT == DT_BF16) reinterpret_cast<uint16_t*>(out)[idx] = (uint16_t)f32_to_bf16_bits(v);
+  else reinterpret_cast<float*>(out)[idx] = v;
+}
+
+template <int DOUT>
 __device__ __forceinline__ void store_entry8(const SoftAcc (&acc)[8], char* dst) {
   float o[8];
 #pragma unroll
@@ -291,6 +297,115 @@ __global__ __launch_bounds__(kPoolThreads) void pool_hca_kernel(
   }
 }
 
+// HCA for m <= 128, reading whole rows: a persistent workgroup of 8 waves
+// takes a tile of epe = 8 / wpe entries of one sequence at a time (wpe =
+// ceil(m / 16) waves per entry); wave w covers rows [16 (w % wpe),
+// 16 (w % wpe) + 16) of entry w / wpe and lane l channels [8 l, 8 l + 8) of
+// the workgroup's 512-channel slice, so one load instruction reads a whole
+// row of Z or C (the read pattern that streams fastest: 6.6 TB/s in a probe
+// against 6.2 TB/s for 8 rows x 128 bytes).  The lane's 16 x 8 biases stay in
+// registers for the whole sweep.  A wave folds its rows into (max, sum,
+// weighted sum) per channel; the states of an entry's waves meet in LDS and
+// thread t merges channel t, in wave order.  Measured on the long-context
+// workload: 6.3 TB/s, against 5.9 TB/s for the 64-channel-slice kernel below.
+constexpr int kHcaRowThreads = 512;
+constexpr int kHcaRowsPerWave = 16;
+
+template <int DIN, int DOUT>
+__global__ __launch_bounds__(kHcaRowThreads) void pool_hca_rows_kernel(
+    const char* __restrict__ C, const char* __restrict__ Z, int64_t ld_bytes, const float* __restrict__ B, int m,
+    int c, const TileRec* __restrict__ tiles, int n_tiles, char* __restrict__ out) {
+  // No FMA contraction of the sums: the normaliser and the numerator take the
+  // same roundings, so value rows of ones give entries of exactly one.
+#pragma clang fp contract(off)
+  constexpr int ES = DTypeSize<DIN>::value;
+  constexpr int OS = DTypeSize<DOUT>::value;
+  constexpr int RC = DIN == DT_BF16 ? 4 : 2;          // rows per load chunk (registers in flight)
+  __shared__ float xs[8][3][kCsaSlice];              // 48 KiB: (M, S, A) of every channel, per wave
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ch0 = blockIdx.y * kCsaSlice;
+  const int width = min(kCsaSlice, c - ch0);
+  const int wpe = (m + kHcaRowsPerWave - 1) / kHcaRowsPerWave;   // waves per entry
+  const int epe = 8 / wpe;                                         // entries per tile
+  const int q = w / wpe, r0 = (w - q * wpe) * kHcaRowsPerWave;     // the wave's entry and first row
+  const bool lane_ok = lane * 8 < width;
+  const int v = lane_ok ? lane : 0;
+  const int64_t col = (int64_t)(ch0 + v * 8) * ES;
+  float bias[kHcaRowsPerWave][8];
+#pragma unroll
+  for (int r = 0; r < kHcaRowsPerWave; ++r) {
+    const int rr = min(r0 + r, m - 1);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bias[r][j] = B[(int64_t)rr * c + ch0 + v * 8 + j] * kLog2e;
+  }
+  for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+    const TileRec t = tiles[tile];
+    const int ne = t.n_rows / m;
+    const bool active = q < epe && q < ne;            // wave-uniform
+    SoftAcc acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) softacc_init(acc[j]);
+    if (active) {
+      const int64_t row0 = (int64_t)t.row_start + (int64_t)q * m;
+#pragma unroll
+      for (int h = 0; h < kHcaRowsPerWave / RC; ++h) {
+        Raw8<DIN> z[RC], x[RC];
+#pragma unroll
+        for (int k = 0; k < RC; ++k) {
+          const int r = min(r0 + h * RC + k, m - 1);  // rows past the block re-read its last row, masked off
+          ld_raw<DIN>(z[k], Z + (row0 + r) * ld_bytes + col);
+          ld_raw<DIN>(x[k], C + (row0 + r) * ld_bytes + col);
+        }
+        float top[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) top[j] = acc[j].M;
+#pragma unroll
+        for (int k = 0; k < RC; ++k) {
+          const bool ok = r0 + h * RC + k < m;
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            top[j] = fmaxf(top[j], ok ? fmaf(raw_get<DIN>(z[k], j), kLog2e, bias[h * RC + k][j]) : -INFINITY);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float sc = exp2_hw(acc[j].M - top[j]);   // 0 while the state is empty
+          acc[j].S *= sc;
+          acc[j].A *= sc;
+          acc[j].M = top[j];
+        }
+#pragma unroll
+        for (int k = 0; k < RC; ++k) {
+          const bool ok = r0 + h * RC + k < m;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float l = fmaf(raw_get<DIN>(z[k], j), kLog2e, bias[h * RC + k][j]);
+            const float wt = exp2_hw((ok ? l : -INFINITY) - top[j]);
+            acc[j].S += wt;
+            acc[j].A = fmaf(wt, raw_get<DIN>(x[k], j), acc[j].A);
+          }
+        }
+      }
+    }
+    __syncthreads();                                   // the previous tile's merges have read xs
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      xs[w][0][lane * 8 + j] = acc[j].M;
+      xs[w][1][lane * 8 + j] = acc[j].S;
+      xs[w][2][lane * 8 + j] = acc[j].A;
+    }
+    __syncthreads();
+    const int ch = threadIdx.x;                        // 512 threads: one channel of the slice each
+    if (ch < width) {
+      for (int e = 0; e < min(epe, ne); ++e) {
+        SoftAcc mg{xs[e * wpe][0][ch], xs[e * wpe][1][ch], xs[e * wpe][2][ch]};
+        for (int u = 1; u < wpe; ++u)
+          mg = softacc_merge(mg, SoftAcc{xs[e * wpe + u][0][ch], xs[e * wpe + u][1][ch], xs[e * wpe + u][2][ch]});
+        store1_pool<DOUT>(out, ((int64_t)(t.entry_start + e) * c + ch0 + ch), mg.A / mg.S);
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_pool_csa(int in_dt, int out_dt, const void* Ca, const void* Cb, const void* Za, const void* Zb,
@@ -316,6 +431,20 @@ hipError_t launch_pool_csa(int in_dt, int out_dt, const void* Ca, const void* Cb
 hipError_t launch_pool_hca(int in_dt, int out_dt, const void* C, const void* Z, int64_t ld_in, const float* B,
                            int m, int c, const TileRec* tiles, int n_tiles, void* out, hipStream_t stream) {
   const int64_t ldb = ld_in * (in_dt == DT_BF16 ? 2 : 4);
+  if (m <= kPoolHcaRowsMaxM) {
+    // one workgroup of 8 waves per compute unit walks the tiles
+    const dim3 grid((unsigned)std::min<int64_t>(n_tiles, device_cu_count()), (c + kCsaSlice - 1) / kCsaSlice),
+        block(kHcaRowThreads);
+    auto args = [&](auto kern) {
+      hipLaunchKernelGGL(kern, grid, block, 0, stream, (const char*)C, (const char*)Z, ldb, B, m, c, tiles, n_tiles,
+                         (char*)out);
+    };
+    if (in_dt == DT_BF16 && out_dt == DT_BF16) args(pool_hca_rows_kernel<DT_BF16, DT_BF16>);
+    else if (in_dt == DT_BF16 && out_dt == DT_F32) args(pool_hca_rows_kernel<DT_BF16, DT_F32>);
+    else if (in_dt == DT_F32 && out_dt == DT_BF16) args(pool_hca_rows_kernel<DT_F32, DT_BF16>);
+    else args(pool_hca_rows_kernel<DT_F32, DT_F32>);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((int64_t)(n_tiles + 7) / 8 * 8 * ((c + kHcaSlice - 1) / kHcaSlice))),
       block(kPoolThreads);
   const size_t lds = (size_t)m * min(c, kHcaSlice) * sizeof(float);      // <= 64 KiB for m <= 256

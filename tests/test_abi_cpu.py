@@ -68,7 +68,10 @@ def test_num_entries_and_workspace(lib):
     tiles = 8192 // 256
     # CSA pooling: tiles of 4 entries (one per wave) at c = 512 -> 512 tiles of 16 rows
     assert lib.seqcomp_workspace_bytes(_lib.OP_POOL_CSA, 0, 4, 512, _p(one), 1, _lib.BF16) == 512 * 16
-    assert lib.seqcomp_workspace_bytes(_lib.OP_POOL_HCA, 0, 128, 512, _p(one), 1, _lib.BF16) == 256   # 16 tiles of 4 entries
+    # HCA pooling, m' = 128: one entry per tile (8 waves of 16 rows) -> 64 tiles
+    assert lib.seqcomp_workspace_bytes(_lib.OP_POOL_HCA, 0, 128, 512, _p(one), 1, _lib.BF16) == 64 * 16
+    # m' = 8: 8 entries per tile -> 128 tiles
+    assert lib.seqcomp_workspace_bytes(_lib.OP_POOL_HCA, 0, 8, 512, _p(one), 1, _lib.BF16) == 128 * 16
     assert lib.seqcomp_workspace_bytes(_lib.OP_POOL_CSA, 0, 4, 512, _p(one), 1, _lib.FP8_E4M3) == 512 * 16 + 2048 * 512 * 4
     # narrower channels: 512 / c entries per wave (c = 128: 16 entries, 64 rows per tile)
     assert lib.seqcomp_workspace_bytes(_lib.OP_POOL_CSA, 0, 4, 128, _p(one), 1, _lib.BF16) == (8192 // 64) * 16
