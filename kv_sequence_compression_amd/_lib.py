@@ -9,7 +9,10 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libseqcomp.so")
+# SEQCOMP_LIBRARY names another build of the same library (the host-sanitized
+# one of the C ABI tests); by default the in-tree libseqcomp.so.
+LIB_PATH = os.environ.get("SEQCOMP_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                              "libseqcomp.so")
 
 # Mirror of the enums in include/seqcomp.h.
 OK = 0

@@ -262,14 +262,6 @@ int fused_impl(int mode, int64_t m, const void* H, int64_t d, int in_dtype, cons
   if (!aligned16(H) || !aligned16(Wt) || !aligned16(Ba) || (csa && !aligned16(Bb)) || !aligned16(cu_seqlens_dev))
     return SEQCOMP_E_ALIGN;
   const WsLayout L = ws_layout(SEQCOMP_OP_FUSED, mode, m, c, cu_seqlens_host, batch, out_dtype);
-  if (use_scratch) {
-    // every check above is host-only; this is the call's first HIP call
-    if (L.total > kScratchBytes) return SEQCOMP_E_SCRATCH;
-    if ((st = device_scratch(&workspace))) return st;
-    workspace_bytes = kScratchBytes;
-  }
-  Range ws_r;
-  if ((st = check_workspace(workspace, workspace_bytes, L.total, &ws_r))) return st;
   const int es = elt_size(in_dtype);
   const int S = csa ? 4 : 2;
   Range reads[5];
@@ -279,6 +271,17 @@ int fused_impl(int mode, int64_t m, const void* H, int64_t d, int in_dtype, cons
   reads[nr++] = range_of(Ba, (size_t)m * c * 4);
   if (csa) reads[nr++] = range_of(Bb, (size_t)m * c * 4);
   reads[nr++] = range_of(cu_seqlens_dev, (size_t)(batch + 1) * 8);
+  if (use_scratch) {
+    // the outputs against the inputs, then the scratch size: all host-side
+    // checks come before the call's first HIP call (the scratch lookup)
+    const Range outs[2] = {out_r, scale_r};
+    if ((st = check_alias(outs, 2, reads, nr))) return st;
+    if (L.total > kScratchBytes) return SEQCOMP_E_SCRATCH;
+    if ((st = device_scratch(&workspace))) return st;
+    workspace_bytes = kScratchBytes;
+  }
+  Range ws_r;
+  if ((st = check_workspace(workspace, workspace_bytes, L.total, &ws_r))) return st;
   const Range writes[3] = {out_r, scale_r, ws_r};
   if ((st = check_alias(writes, 3, reads, nr))) return st;
 

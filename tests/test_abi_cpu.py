@@ -378,3 +378,34 @@ def test_mqa_rejects_bad_arguments(lib, kw, code):
 
 def test_mqa_empty_calls_launch_nothing(lib):
     assert mqa(lib, cu_q=_cu(0, 0), q=0, out=0, lse=0, ws=0, ws_bytes=0) == S["SEQCOMP_OK"]
+
+
+def test_hip_failure_maps_to_e_hip(lib):
+    """A well-formed call passes validation and reaches its first HIP call;
+    on a host with no GPU that call fails and the entry point returns
+    SEQCOMP_E_HIP (the fused call at a kernel launch, the allocation-free one
+    when it looks up the device's scratch)."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("needs a host without a GPU: with one these calls would launch on fake addresses")
+    assert fused(lib) == S["SEQCOMP_E_HIP"]
+    cu = _cu(0, 8192)
+    assert lib.seqcomp_compress_fused_noalloc(_lib.MODE_CSA, 4, A, 7168, _lib.BF16, B_, 512, BIAS, BIAS2, _p(cu), CU_DEV,
+                                              1, OUT, _lib.BF16, 0, None) == S["SEQCOMP_E_HIP"]
+
+
+def test_noalloc_rejects_beyond_its_scratch(lib):
+    """The allocation-free call rejects, before any HIP call, a batch whose
+    workspace would exceed its 64 MiB (fp8 staging of 200704 tokens at
+    c = 512), and validates its other arguments like the workspace form."""
+    cu = _cu(0, 200704)
+    f = lib.seqcomp_compress_fused_noalloc
+    assert f(_lib.MODE_CSA, 4, A, 64, _lib.BF16, B_, 512, BIAS, BIAS2, _p(cu), CU_DEV, 1, OUT, _lib.FP8_E4M3, SCALE,
+             None) == S["SEQCOMP_E_SCRATCH"]
+    one = _cu(0, 8192)
+    assert f(_lib.MODE_CSA, 3, A, 7168, _lib.BF16, B_, 512, BIAS, BIAS2, _p(one), CU_DEV, 1, OUT, _lib.BF16, 0,
+             None) == S["SEQCOMP_E_UNSUPPORTED"]
+    assert f(_lib.MODE_CSA, 4, 0, 7168, _lib.BF16, B_, 512, BIAS, BIAS2, _p(one), CU_DEV, 1, OUT, _lib.BF16, 0,
+             None) == S["SEQCOMP_E_NULL"]
+    assert f(_lib.MODE_CSA, 4, A, 7168, _lib.BF16, B_, 512, BIAS, BIAS2, _p(one), CU_DEV, 1, A + 4096, _lib.BF16, 0,
+             None) == S["SEQCOMP_E_ALIAS"]
