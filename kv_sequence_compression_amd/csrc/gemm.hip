@@ -384,12 +384,12 @@ __device__ __forceinline__ int b_row_of(int n, int nt, int c, int n_out) {
 
 // Softmax partial of the 4 rows of run q (elements 4 q .. 4 q + 3) of one
 // accumulator: logits z + B in log2 units (bias2 = log2(e) * B), values v.
-__device__ __forceinline__ SoftAcc partial4(const f32x16_t& z, const f32x16_t& v, int q, const float (&bias2)[4]) {
+__device__ __forceinline__ SoftAcc partial_rows4(const float (&z)[4], const float (&v)[4], const float (&bias2)[4]) {
   float l[4];
   float M = -INFINITY;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    l[j] = fmaf(z[4 * q + j], kLog2e, bias2[j]);
+    l[j] = fmaf(z[j], kLog2e, bias2[j]);
     M = fmaxf(M, l[j]);
   }
   SoftAcc s;
@@ -400,9 +400,14 @@ __device__ __forceinline__ SoftAcc partial4(const f32x16_t& z, const f32x16_t& v
   for (int j = 0; j < 4; ++j) {
     const float w = exp2_hw(l[j] - M);
     s.S += w;
-    s.A = fmaf(w, v[4 * q + j], s.A);
+    s.A = fmaf(w, v[j], s.A);
   }
   return s;
+}
+__device__ __forceinline__ SoftAcc partial4(const f32x16_t& z, const f32x16_t& v, int q, const float (&bias2)[4]) {
+  const float zq[4] = {z[4 * q], z[4 * q + 1], z[4 * q + 2], z[4 * q + 3]};
+  const float vq[4] = {v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+  return partial_rows4(zq, vq, bias2);
 }
 
 // The partial of lane l ^ 32 (the other lane half, same column), through the
@@ -1059,6 +1064,7 @@ __global__ __launch_bounds__(kSkThreads, 1) void append_skinny_kernel(Args a, in
     sk_epilogue<DOUT>(a, acc, mt, nt, w, lane);
     return;
   }
+  if ((int64_t)mt * 32 + w * 8 >= a.nb) return;           // no block of row block w: nothing reads it
   float4* dst = partial + (((int64_t)L * S + sp) * 4 + w) * kSkPartialQuads + lane;
 #pragma unroll
   for (int jn = 0; jn < 4; ++jn)
@@ -1080,54 +1086,69 @@ __global__ __launch_bounds__(kSkThreads, 1) void append_skinny_kernel(Args a, in
 // adds splits u, u + 8, ... in increasing order, then the waves' sums meet in
 // a fixed tree through LDS ((4..7 into 0..3), (2, 3 into 0, 1), 1 into 0 --
 // the same sum on every call) and wave 0 runs the append epilogue.
+// Reduce of the skinny split-K.  Workgroup (tile L, row block rb, run q)
+// owns blocks j = 32 mt + 8 rb + 2 q + h (h = lane / 32) of the tile's 32
+// channels: wave u adds stream u's float4 (the 4 rows of the lane's block)
+// over the S splits in split order, every load issued before the first add;
+// waves 1..3 hand their sums to wave 0 through LDS, and wave 0, whose
+// epilogue inputs were loaded before the partials, finishes the run.
+constexpr int kSkReduceThreads = 256;
+constexpr int kSkReduceUnroll = 8;
 template <int DOUT>
-__global__ __launch_bounds__(kSkThreads) void append_skinny_reduce_kernel(Args a, int S,
-                                                                          const float4* __restrict__ partial) {
-  __shared__ float4 xch[4][16][64];                  // 64 KiB
-  const int L = blockIdx.x >> 2, w = blockIdx.x & 3;
-  const int u = threadIdx.x >> 6, lane = threadIdx.x & 63;
+__global__ __launch_bounds__(kSkReduceThreads) void append_skinny_reduce_kernel(Args a, int S,
+                                                                                const float4* __restrict__ partial) {
+  __shared__ float4 xch[3][64];
+  const int q = blockIdx.x & 3, rb = (blockIdx.x >> 2) & 3, L = blockIdx.x >> 4;
+  const int u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int mt = L / a.n_nt, nt = L - mt * a.n_nt;
-  float4 sum[16];
+  const int64_t jrun = (int64_t)mt * 32 + rb * 8 + 2 * q;
+  if (jrun >= a.nb) return;                                // both blocks of the run are past the batch
+  const int col = lane & 31, h = lane >> 5;
+  const int ch = nt * 32 + col;
+  const int chc = min(ch, a.c - 1);
+  const int64_t j = jrun + h;
+  float ba[4] = {}, bb[4] = {}, st[3] = {};   // scaled by log2(e) after the sums: no wait before the partials
+  if (u == 0) {
 #pragma unroll
-  for (int k = 0; k < 16; ++k) sum[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int sp = u; sp < S; sp += 8) {
-    const float4* src = partial + (((int64_t)L * S + sp) * 4 + w) * kSkPartialQuads + lane;
-    float4 v[16];
+    for (int r = 0; r < 4; ++r) {
+      ba[r] = a.Ba[r * a.c + chc];
+      bb[r] = a.Bb[r * a.c + chc];
+    }
+    const float* sp = a.state_in + min(j, a.nb - 1) * 3 * a.c + chc;
+    st[0] = sp[0];
+    st[1] = sp[a.c];
+    st[2] = sp[2 * a.c];
+  }
+  // split sp of this (tile, row block) sits at + sp * 4 * kSkPartialQuads
+  const float4* src = partial + ((int64_t)L * S * 4 + rb) * kSkPartialQuads + (u * 4 + q) * 64 + lane;
+  float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < S; s0 += kSkReduceUnroll) {
+    float4 v[kSkReduceUnroll];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) v[k] = src[k * 64];
+    for (int i = 0; i < kSkReduceUnroll; ++i)   // unconditional (clamped) loads: no wait between them
+      v[i] = src[(int64_t)min(s0 + i, S - 1) * 4 * kSkPartialQuads];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      sum[k].x += v[k].x; sum[k].y += v[k].y; sum[k].z += v[k].z; sum[k].w += v[k].w;
+    for (int i = 0; i < kSkReduceUnroll; ++i) {
+      const bool in = s0 + i < S;
+      sum.x += in ? v[i].x : 0.f;
+      sum.y += in ? v[i].y : 0.f;
+      sum.z += in ? v[i].z : 0.f;
+      sum.w += in ? v[i].w : 0.f;
     }
   }
-#pragma unroll
-  for (int half = 4; half >= 1; half >>= 1) {
-    if (u >= half && u < 2 * half) {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) xch[u - half][k][lane] = sum[k];
-    }
-    __syncthreads();
-    if (u < half) {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const float4 o = xch[u][k][lane];
-        sum[k].x += o.x; sum[k].y += o.y; sum[k].z += o.z; sum[k].w += o.w;
-      }
-    }
-    __syncthreads();
-  }
+  if (u > 0) xch[u - 1][lane] = sum;
+  __syncthreads();
   if (u != 0) return;
-  f32x16_t acc[4];
 #pragma unroll
-  for (int jn = 0; jn < 4; ++jn)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      acc[jn][4 * q4 + 0] = sum[jn * 4 + q4].x;
-      acc[jn][4 * q4 + 1] = sum[jn * 4 + q4].y;
-      acc[jn][4 * q4 + 2] = sum[jn * 4 + q4].z;
-      acc[jn][4 * q4 + 3] = sum[jn * 4 + q4].w;
-    }
-  sk_epilogue<DOUT>(a, acc, mt, nt, w, lane);
+  for (int r = 0; r < 4; ++r) {
+    ba[r] *= kLog2e;
+    bb[r] *= kLog2e;
+  }
+  const float4 cb = xch[0][lane], za4 = xch[1][lane], zb4 = xch[2][lane];
+  const float va[4] = {sum.x, sum.y, sum.z, sum.w}, vb[4] = {cb.x, cb.y, cb.z, cb.w};
+  const float za[4] = {za4.x, za4.y, za4.z, za4.w}, zb[4] = {zb4.x, zb4.y, zb4.z, zb4.w};
+  append_store<DOUT>(a, partial_rows4(za, va, ba), partial_rows4(zb, vb, bb), SoftAcc{st[0], st[1], st[2]}, j,
+                     ch < a.c, ch);
 }
 
 // Form of a decode append of nb blocks:
@@ -1141,7 +1162,115 @@ __global__ __launch_bounds__(kSkThreads) void append_skinny_reduce_kernel(Args a
 //    256 x 256 tiles split 16 ways).
 // S is capped at the K loop's slab count nk.  A function of nb, c and nk
 // only, so the workspace size does not depend on the device.
-enum AppendForm { APPEND_BIG = 0, APPEND_BIG_SPLIT = 1, APPEND_SKINNY = 2 };
+// Decode append for one or two sequences (4 nb <= 8 rows of H): no tiles
+// and no partial products, one launch.  A workgroup of 8 waves owns
+// channels 2 g and 2 g + 1; wave w dots weight row (w % 4) c + 2 g + w / 4
+// (stream w % 4 of its channel, in the row order C^a, C^b, Z^a, Z^b of Wt)
+// with every row of H.  K advances in pieces of 16 KiB of each row: H's
+// piece is staged in LDS once for the 8 waves, lane l of a wave takes the
+// 16-byte chunks l + 64 i of the piece, and every load of a piece is issued
+// before the first is used.  The 8 x R dot products meet in LDS and 2 nb
+// threads run the append epilogue.  At c = 512 the 256 workgroups stream
+// the weights once; the MFMA tiles would read 16 to 32 x as many H rows as
+// there are and need a split-K round trip to fill the chip.
+constexpr int kGvThreads = 512;
+constexpr int kGvPieceChunks = 16;                        // 16-byte chunks per lane and piece
+constexpr int kGvPieceRowChunks = kGvPieceChunks * 64;    // 16 KiB of each row per piece
+constexpr int kGvMaxBlocks = 2;
+
+// acc + <w, h> over one 16-byte chunk (8 bf16 or 4 fp32 of each operand).
+template <int DIN>
+__device__ __forceinline__ float dot_chunk(const f32x4_t& w, const f32x4_t& h, float acc) {
+  if (DIN == DT_BF16) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      // the elements go through scalars: hipcc bit-casts a subscripted vector
+      // element as if it were element 0
+      const float wt = w[t], ht = h[t];
+      // v_dot2c_f32_bf16: acc + w0 h0 + w1 h1 (bf16 products are exact in fp32)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, wt), __builtin_bit_cast(bf16x2_t, ht), acc,
+                                            false);
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc = fmaf(w[t], h[t], acc);
+  }
+  return acc;
+}
+
+template <int DIN, int DOUT, int R>
+__global__ __launch_bounds__(kGvThreads, 1) void append_gemv_kernel(Args a) {
+  __shared__ f32x4_t hs[R][kGvPieceRowChunks];              // R x 16 KiB
+  __shared__ float red[8][R];
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int ch = 2 * blockIdx.x + (w >> 2);                // c is even: ch < c
+  const int nck = (int)(a.lda >> 4);                       // 16-byte chunks per row
+  const f32x4_t* wrow = reinterpret_cast<const f32x4_t*>(a.Wt + (int64_t)((w & 3) * a.c + ch) * a.lda);
+  const f32x4_t* hsrc = reinterpret_cast<const f32x4_t*>(a.H);
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+  for (int p0 = 0; p0 < nck; p0 += kGvPieceRowChunks) {
+    const int pn = min(kGvPieceRowChunks, nck - p0);       // chunks of each row in this piece
+    // H first, then this wave's weight chunks, all unconditional (a chunk
+    // past the piece reads the row's last one: branches around the loads
+    // would serialise them), so the H stores below wait for the H loads only
+    f32x4_t hv[2 * R];
+#pragma unroll
+    for (int i = 0; i < 2 * R; ++i) {
+      const int f = tid + kGvThreads * i, r = f / kGvPieceRowChunks, k = f % kGvPieceRowChunks;
+      hv[i] = hsrc[(int64_t)r * nck + p0 + min(k, pn - 1)];
+    }
+    f32x4_t wv[kGvPieceChunks];
+#pragma unroll
+    for (int i = 0; i < kGvPieceChunks; ++i)
+      wv[i] = __builtin_nontemporal_load(wrow + p0 + min(lane + 64 * i, pn - 1));
+#pragma unroll
+    for (int i = 0; i < kGvPieceChunks; ++i)   // chunks past the piece add 0 x (a finite copy of an H chunk)
+      if (lane + 64 * i >= pn) wv[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (p0 > 0) __syncthreads();                           // every wave is done with the previous piece
+#pragma unroll
+    for (int i = 0; i < 2 * R; ++i) {
+      const int f = tid + kGvThreads * i;
+      hs[f / kGvPieceRowChunks][f % kGvPieceRowChunks] = hv[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kGvPieceChunks; ++i) {
+      const int k = lane + 64 * i;
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = dot_chunk<DIN>(wv[i], hs[r][k], acc[r]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float v = acc[r];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    if (lane == 0) red[w][r] = v;
+  }
+  __syncthreads();
+  if (tid >= 2 * a.nb) return;
+  const int j = tid >> 1, cc = tid & 1;                    // block j of channel 2 g + cc
+  const int chj = 2 * blockIdx.x + cc;
+  float za[4], va[4], zb[4], vb[4], ba[4], bb[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    va[t] = red[cc * 4 + 0][4 * j + t];
+    vb[t] = red[cc * 4 + 1][4 * j + t];
+    za[t] = red[cc * 4 + 2][4 * j + t];
+    zb[t] = red[cc * 4 + 3][4 * j + t];
+    ba[t] = a.Ba[t * a.c + chj] * kLog2e;
+    bb[t] = a.Bb[t * a.c + chj] * kLog2e;
+  }
+  const float* st = a.state_in + (int64_t)j * 3 * a.c + chj;
+  const SoftAcc prev{st[0], st[a.c], st[2 * a.c]};
+  append_store<DOUT>(a, partial_rows4(za, va, ba), partial_rows4(zb, vb, bb), prev, j, true, chj);
+}
+
+enum AppendForm { APPEND_BIG = 0, APPEND_BIG_SPLIT = 1, APPEND_SKINNY = 2, APPEND_GEMV = 3 };
 struct AppendPlan {
   int form;
   int S;
@@ -1152,7 +1281,11 @@ AppendPlan append_plan(int64_t nb, int c, int nk) {
   AppendPlan p{};
   const int64_t gb = big_append_tiles(nb, c);
   int64_t S;
-  if (gb >= kAppendWorkgroups) {
+  if (nb <= kGvMaxBlocks) {
+    p.form = APPEND_GEMV;
+    p.tiles = c / 2;
+    S = 1;
+  } else if (gb >= kAppendWorkgroups) {
     p.form = APPEND_BIG;
     p.tiles = gb;
     S = 1;
@@ -1263,6 +1396,19 @@ hipError_t launch_csa_append(int in_dt, int out_dt, const void* H, int64_t nb, i
   const int G = (int)p.tiles, S = p.S;
   if (S > 1 && partial == nullptr) return hipErrorInvalidValue;
   float4* part = static_cast<float4*>(partial);
+  if (p.form == APPEND_GEMV) {
+    auto gemv = [&](auto kern) { hipLaunchKernelGGL(kern, dim3(G), dim3(kGvThreads), 0, stream, a); };
+    if (nb == 1) {
+      if (in_dt == DT_BF16) out_dt == DT_BF16 ? gemv(append_gemv_kernel<DT_BF16, DT_BF16, 4>)
+                                              : gemv(append_gemv_kernel<DT_BF16, DT_F32, 4>);
+      else out_dt == DT_BF16 ? gemv(append_gemv_kernel<DT_F32, DT_BF16, 4>) : gemv(append_gemv_kernel<DT_F32, DT_F32, 4>);
+    } else {
+      if (in_dt == DT_BF16) out_dt == DT_BF16 ? gemv(append_gemv_kernel<DT_BF16, DT_BF16, 8>)
+                                              : gemv(append_gemv_kernel<DT_BF16, DT_F32, 8>);
+      else out_dt == DT_BF16 ? gemv(append_gemv_kernel<DT_F32, DT_BF16, 8>) : gemv(append_gemv_kernel<DT_F32, DT_F32, 8>);
+    }
+    return hipGetLastError();
+  }
   if (p.form != APPEND_SKINNY) {
     a.n_mt = (int)((a.T + kTile - 1) / kTile);
     a.n_nt = (c + 63) / 64;
@@ -1288,9 +1434,11 @@ hipError_t launch_csa_append(int in_dt, int out_dt, const void* H, int64_t nb, i
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   if (out_dt == DT_BF16)
-    hipLaunchKernelGGL(append_skinny_reduce_kernel<DT_BF16>, dim3(G * 4), dim3(kSkThreads), 0, stream, a, S, part);
+    hipLaunchKernelGGL(append_skinny_reduce_kernel<DT_BF16>, dim3(G * 16), dim3(kSkReduceThreads), 0, stream, a, S,
+                       part);
   else
-    hipLaunchKernelGGL(append_skinny_reduce_kernel<DT_F32>, dim3(G * 4), dim3(kSkThreads), 0, stream, a, S, part);
+    hipLaunchKernelGGL(append_skinny_reduce_kernel<DT_F32>, dim3(G * 16), dim3(kSkReduceThreads), 0, stream, a, S,
+                       part);
   return hipGetLastError();
 }
 

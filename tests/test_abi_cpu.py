@@ -194,8 +194,13 @@ def test_append_workspace(lib):
     # 100 blocks: 4 x 16 tiles, 4 ways; fp8 adds the fp32 staging of the entries
     assert f(100, 512, _lib.BF16) == 64 * 4 * part
     assert f(100, 512, _lib.FP8_E4M3) == 64 * 4 * part + 100 * 512 * 4
-    # 1 block: 16 tiles, 16 ways; c = 160 (5 channel tiles): 5 tiles, capped at 32 ways
-    assert f(1, 512, _lib.BF16) == 16 * 16 * part
+    # 1 or 2 blocks: one weight row per wave, no tiles and no partials (fp8
+    # keeps its staging); 3 blocks: 16 tiles, 16 ways
+    assert f(1, 512, _lib.BF16) == 0
+    assert f(2, 512, _lib.BF16) == 0
+    assert f(2, 512, _lib.FP8_E4M3) == 2 * 512 * 4
+    assert f(3, 512, _lib.BF16) == 16 * 16 * part
+    # c = 160 (5 channel tiles): 5 tiles, capped at 32 ways
     assert f(20, 160, _lib.BF16) == 5 * 32 * part
     # 400 blocks: 7 x 8 tiles of 256 x 256 are too few, 13 x 16 = 208 of 128 x 128 run unsplit
     assert f(400, 512, _lib.BF16) == 0

@@ -141,6 +141,39 @@ def test_append_big_tile_split(gpu_device):
     assert max_abs_err(to64(out), ref) <= 2e-5
 
 
+@pytest.mark.parametrize("nseq", [1, 2])
+def test_append_few_sequences_full_depth(gpu_device, nseq):
+    """One or two sequences (the one-launch kernel with a wave per weight
+    row) at d = 7168, bf16 operands, c = 512: fp32 entries against the
+    oracle at 1e-5 of each row's largest entry (products exact in fp32, sums
+    over 7168 terms), then bf16 entries in place and fp8 entries."""
+    case = synth.compressor_case("csa", [12] * nseq, 7168, 512, 4, seed=20 + nseq, in_dtype="bf16", bias_std=0.3,
+                                 device=gpu_device)
+    ref = _oracle(case)
+    out, _ = _append_all(case, "f32", in_place=False)
+    err = row_rel_err(to64(out), ref).max()
+    print(f"nseq={nseq}: fp32 entries from bf16 operands, max row-relative error {err:.3e}")
+    assert err <= 1e-5
+    out, _ = _append_all(case, "bf16", in_place=True)
+    assert row_rel_err(to64(out), ref).max() <= 2 ** -8
+    q, s = _append_all(case, "fp8", in_place=False)
+    check_fp8(q, s, ref, 2 ** -8)
+
+
+@pytest.mark.parametrize("nseq,d,c", [(1, 8192, 48), (2, 8192, 16), (2, 4160, 32)])
+def test_append_few_sequences_fp32_pieces(gpu_device, nseq, d, c):
+    """fp32 operands: a row of d = 8192 is two 16 KiB pieces (the second one
+    full), d = 4160 two pieces with a ragged second (64 of 1024 chunks);
+    c = 16 is a grid of 8 workgroups."""
+    case = synth.compressor_case("csa", [8] * nseq, d, c, 4, seed=30 + d + c, in_dtype="f32", bias_std=0.5,
+                                 device=gpu_device)
+    ref = _oracle(case)
+    out, _ = _append_all(case, "f32", in_place=nseq == 2)
+    err = max_abs_err(to64(out), ref)
+    print(f"nseq={nseq} d={d} c={c}: max abs error {err:.3e}")
+    assert err <= 2e-5
+
+
 def test_append_agrees_with_fused(gpu_device):
     """One append of every sequence's second block, fed the state of its first
     block, equals entry 1 of the fused compressor over the two blocks."""
