@@ -210,14 +210,15 @@ int seqcomp_compress_fused_noalloc(int mode, int64_t m, const void* H, int64_t d
  *             the sequence's next append.  May be the same pointer as
  *             state_in (updated in place); must not overlap it otherwise.
  *   out       [nb x c] of out_dtype; out_scale [nb] fp32 for fp8 output.
- *   workspace seqcomp_append_workspace_bytes(nb, c, out_dtype) bytes: when
- *             the batch's 256 x 256 tiles (64 channels x 4 streams) do not
- *             fill 256 workgroups, it runs 128 x 128 tiles (32 channels x 4
- *             streams) and, if those are fewer than 256 too, splits the K
- *             loop over up to 32 workgroups per tile; their fp32 partial
- *             products take 64 KiB per tile and split (16 MiB at nb = 64,
- *             c = 512); for an fp8 output, nb x c fp32 of staging.  0 when
- *             neither applies.
+ *   workspace seqcomp_append_workspace_bytes(nb, c, out_dtype) bytes.
+ *             nb <= 2 runs one kernel with a wave per weight row and needs
+ *             none.  Otherwise, when the batch's 256 x 256 tiles (64
+ *             channels x 4 streams) do not fill 256 workgroups, it runs
+ *             128 x 128 tiles (32 channels x 4 streams) and, if those are
+ *             fewer than 256 too, splits the K loop over up to 32 workgroups
+ *             per tile; their fp32 partial products take 64 KiB per tile and
+ *             split (16 MiB at nb = 64, c = 512).  An fp8 output adds nb x c
+ *             fp32 of staging.  0 when neither applies.
  *   Requires d % 64 == 0, c % 16 == 0.  nb == 0 returns SEQCOMP_OK.
  * Appending a sequence's blocks one call at a time gives the same entries as
  * seqcomp_compress_fused over the whole sequence (up to rounding order).

@@ -63,9 +63,10 @@ hipError_t launch_fused(int mode, int in_dt, int out_dt, const void* H, int d, c
 
 // CSA decode append: nb independent blocks of 4 rows of H; entry j merges
 // block j's a-partial with state_in[j] (the previous block's b-partial, fp32
-// [nb][3][c]) and block j's b-partial goes to state_out[j].  Batches whose
-// 256 x 256 tiles fill the chip run the big-tile kernel; smaller ones run
-// 128 x 128 tiles with the K loop split over up to 32 workgroups per tile,
+// [nb][3][c]) and block j's b-partial goes to state_out[j].  One or two
+// blocks run a kernel with a wave per weight row; batches whose 256 x 256
+// tiles fill the chip run the big-tile kernel; the others run 128 x 128
+// tiles with the K loop split over up to 32 workgroups per tile,
 // `partial` (append_partial_bytes(nb, c) bytes, null when that is 0)
 // holding their fp32 products until a reduce kernel adds them and runs the
 // same epilogue.
