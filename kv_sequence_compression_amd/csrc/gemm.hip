@@ -806,50 +806,73 @@ __global__ __launch_bounds__(kThreads, 1) void append_splitk_kernel(Args a, int 
 // Workgroup = one wave: (tile L, wave w, M subtile ms).  Four splits' loads
 // are in flight at a time; the sum runs in split order, so it is the same on
 // every call.
+// Adds the U >= S splits' partials of one (tile, wave, row block) in split
+// order, every load issued before the first add (splits past S load split
+// S - 1 again and add nothing).
+template <int U>
+__device__ __forceinline__ void sum_big_partials(const float4* __restrict__ partial, int64_t L, int S, int w, int ms,
+                                                 int lane, f32x16_t (&acc)[4]) {
+  float4 v[U][16];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const float4* src = partial + partial_base(L, S, min(u, S - 1), w, ms) + lane;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v[u][k] = src[k * 64];
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const bool in = u < S;
+#pragma unroll
+    for (int jn = 0; jn < 4; ++jn)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 x = v[u][jn * 4 + q4];
+        acc[jn][4 * q4 + 0] += in ? x.x : 0.f;
+        acc[jn][4 * q4 + 1] += in ? x.y : 0.f;
+        acc[jn][4 * q4 + 2] += in ? x.z : 0.f;
+        acc[jn][4 * q4 + 3] += in ? x.w : 0.f;
+      }
+  }
+}
+
+// Reduce of the big-tile split-K (S <= 4 splits): one wave per (tile, wave
+// of the tile, row block of 8 blocks); the epilogue inputs are loaded before
+// the partials.
 template <int DOUT>
 __global__ __launch_bounds__(64) void append_reduce_kernel(Args a, int S, const float4* __restrict__ partial) {
   const int L = blockIdx.x >> 4, w = (blockIdx.x >> 2) & 3, ms = blockIdx.x & 3;
   const int lane = threadIdx.x;
   const int mt = L / a.n_nt, nt = L - mt * a.n_nt;
   const int wm = w >> 1, wn = w & 1;
-  f32x16_t acc[4];
-#pragma unroll
-  for (int jn = 0; jn < 4; ++jn) acc[jn] = f32x16_t{};
-  for (int s0 = 0; s0 < S; s0 += 4) {
-    float4 v[4][16];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float4* src = partial + partial_base(L, S, min(s0 + u, S - 1), w, ms) + lane;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) v[u][k] = src[k * 64];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (s0 + u < S) {
-#pragma unroll
-        for (int jn = 0; jn < 4; ++jn)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            acc[jn][4 * q4 + 0] += v[u][jn * 4 + q4].x;
-            acc[jn][4 * q4 + 1] += v[u][jn * 4 + q4].y;
-            acc[jn][4 * q4 + 2] += v[u][jn * 4 + q4].z;
-            acc[jn][4 * q4 + 3] += v[u][jn * 4 + q4].w;
-          }
-      }
-    }
-  }
-  float ba[4], bb[4];
-  csa_bias(a, nt, lane, wn, ba, bb);
   const int col = lane & 31, h = lane >> 5;
   const int ch = nt * 64 + wn * 32 + col;
   const bool ok = ch < a.c;
+  const int chc = min(ch, a.c - 1);
   const int64_t j0 = (int64_t)mt * 64 + wm * 32 + ms * 8 + h;
+  float ba[4], bb[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    ba[r] = a.Ba[r * a.c + chc];   // scaled by log2(e) after the sums
+    bb[r] = a.Bb[r * a.c + chc];
+  }
   SoftAcc prev[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int64_t j = min(j0 + q * 2, a.nb - 1);
-    const float* st = a.state_in + j * 3 * a.c + min(ch, a.c - 1);
+    const float* st = a.state_in + j * 3 * a.c + chc;
     prev[q] = SoftAcc{st[0], st[a.c], st[2 * a.c]};
+  }
+  f32x16_t acc[4];
+#pragma unroll
+  for (int jn = 0; jn < 4; ++jn) acc[jn] = f32x16_t{};
+  if (S <= 2)
+    sum_big_partials<2>(partial, L, S, w, ms, lane, acc);
+  else
+    sum_big_partials<4>(partial, L, S, w, ms, lane, acc);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    ba[r] = ok ? ba[r] * kLog2e : 0.f;
+    bb[r] = ok ? bb[r] * kLog2e : 0.f;
   }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -1413,6 +1436,7 @@ hipError_t launch_csa_append(int in_dt, int out_dt, const void* H, int64_t nb, i
     a.n_mt = (int)((a.T + kTile - 1) / kTile);
     a.n_nt = (c + 63) / 64;
     if (S == 1) return dispatch<MODE_CSA_APPEND>(in_dt, out_dt, a, stream);
+    if (S > 4) return hipErrorInvalidValue;   // 64 <= tiles < 256 give S <= 4, all append_reduce_kernel adds
     if (in_dt == DT_BF16)
       hipLaunchKernelGGL(append_splitk_kernel<DT_BF16>, dim3(G * S), dim3(kThreads), 0, stream, a, S, part);
     else
