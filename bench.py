@@ -332,11 +332,14 @@ def decode_append(sc, torch, csa, batches, steps, reps=5):
     captured in a HIP graph, replayed `reps` times between two events (the
     library launches kernels only: no copies, fills or synchronisations).
     `us_eager` is the rate of the same calls made one by one from Python,
-    binding overhead included."""
+    binding overhead included.  `hipblaslt_mm_us` times torch.mm on the
+    projection alone (same rows and weights, bf16 out) the same way: a
+    yardstick for the skinny product, with no pooling or state."""
     d = csa.H.shape[1]
     c = csa.c
     b = csa.biases
     res = {}
+    Wdn = csa.Wt_cat.t().contiguous()
     for nb in batches:
         H = csa.H[: 4 * nb]
         state = sc.csa_empty_state(nb, c, H.device)
@@ -363,9 +366,28 @@ def decode_append(sc, torch, csa, batches, steps, reps=5):
         torch.cuda.synchronize()
         ms = ev[0].elapsed_time(ev[1]) / (reps * steps)
         del g
+        # yardstick: torch.mm (hipBLASLt) on the projection alone, same
+        # graph-replay timing, no pooling
+        Yr = torch.empty((4 * nb, 4 * c), dtype=torch.bfloat16, device=H.device)
+        blas = lambda: torch.mm(H, Wdn, out=Yr)
+        blas()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(steps):
+                blas()
+        g.replay()
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(reps):
+            g.replay()
+        ev[1].record()
+        torch.cuda.synchronize()
+        blas_ms = ev[0].elapsed_time(ev[1]) / (reps * steps)
+        del g
         flops = 2.0 * 4 * nb * d * 4 * c
         wbytes = 4 * c * d * 2 + 4 * nb * d * 2          # weights + new hidden rows
-        res[f"nb={nb}"] = {"us": ms * 1e3, "us_eager": eager_ms * 1e3, "entries_per_s": nb / (ms * 1e-3),
+        res[f"nb={nb}"] = {"us": ms * 1e3, "us_eager": eager_ms * 1e3, "hipblaslt_mm_us": blas_ms * 1e3,
+                           "entries_per_s": nb / (ms * 1e-3),
                            "mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                            "hbm_frac": wbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
     return {"workload": f"CSA decode append, m=4, d={d}, c={c}: one new block per sequence, bf16 out, "

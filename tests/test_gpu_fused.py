@@ -126,6 +126,42 @@ def test_fused_fp32_multitile(gpu_device, mode, lengths, d, c):
     assert max_abs_err(to64(out), ref) <= 2e-5
 
 
+@pytest.mark.parametrize("mode,lengths,d,c", [
+    ("csa", [700, 3, 260, 1025, 4], 128, 80),       # two K slabs, halo fix-up, partial N tile
+    ("csa", [256, 256, 512], 64, 64),                # one K slab, tile-aligned sequences
+    ("csa", [513, 1, 300], 320, 192),                # five K slabs, three N tiles
+    ("hca", [600, 100, 1000, 384], 128, 144),        # partial tiles, dropped tails, partial N tile
+    ("hca", [128, 256], 320, 32),
+])
+def test_fused_bf16_operands_multitile(gpu_device, mode, lengths, d, c):
+    """bf16 operands, fp32 entries, packed batches with ragged tiles.  bf16
+    products are exact in fp32 and the oracle takes the same bf16 values, so
+    only the fp32 accumulation over d <= 320 differs: max abs <= 2e-5, as for
+    fp32 operands (bias std 0.5, so a slip in the epilogue's bias or block
+    bookkeeping cannot hide)."""
+    m = 4 if mode == "csa" else 128
+    case = synth.compressor_case(mode, lengths, d, c, m, seed=5, in_dtype="bf16", bias_std=0.5, device=gpu_device)
+    out, _ = _run(case, "f32")
+    ref = _oracle_full(case)
+    assert out.shape == ref.shape
+    err = max_abs_err(to64(out), ref)
+    print(f"{mode} bf16 operands d={d} c={c}: max abs err {err:.3e}")
+    assert err <= 2e-5
+
+
+@pytest.mark.parametrize("T,d,n_out", [(300, 128, 96), (513, 320, 272), (64, 64, 512)])
+def test_project_bf16_operands_f32_out(gpu_device, T, d, n_out):
+    """bf16 projection with fp32 output against the float64 product of the same
+    bf16 values: max abs <= 2e-5 (exact products, fp32 sums over d <= 320);
+    ragged M and N tiles and one to five K slabs."""
+    H = synth.normal((T, d), 1.0, (12, 1), gpu_device, "bf16")
+    Wt = synth.normal((n_out, d), 1.0 / np.sqrt(d), (12, 2), gpu_device, "bf16")
+    Y = sc.project(H, Wt, "f32")
+    ref = oracle.project(to64(H), to64(Wt).T)
+    assert Y.shape == (T, n_out)
+    assert max_abs_err(to64(Y), ref) <= 2e-5
+
+
 def test_fused_zero_entries(gpu_device):
     """A batch whose sequences are all shorter than m gives an empty result."""
     case = synth.compressor_case("hca", [100, 27], 64, 32, 128, in_dtype="f32", device=gpu_device)
