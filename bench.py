@@ -21,6 +21,8 @@ Prints ONE JSON line (rank 0).  `value` is compressed entries/s of the step
   2^20 x 512; CSA m=4 and HCA m'=128), HBM-bound;
 * the next-row kernels (indexer keys, decode append, RoPE store, lightning
   indexer, HCA dense attention);
+* device: the GPU's properties and a measured 1 GiB device-to-device copy
+  rate, beside the published peaks the fractions use;
 * cpu_baseline: the float64 oracle on a bounded sample of the same workload
   (the first 262144 tokens of the batch) on this host's cores, the same on
   one core, and per workload (tiny, csa_full, hca_full, pooling) with all
@@ -118,6 +120,28 @@ def _time_calls(torch, calls, steps: int, warmup: int = 2):
     torch.cuda.synchronize()
     t = np.array([ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(steps)])
     return float(np.median(t)), float(t.min()), float(t.mean())
+
+
+def device_record(torch, dev):
+    """The device's properties and a measured plain device-to-device copy of
+    1 GiB (torch copy: 1 GiB read + 1 GiB written), beside the published
+    peaks the roofline fractions use."""
+    p = torch.cuda.get_device_properties(dev)
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    src.fill_(1.0)
+    dst = torch.empty_like(src)
+    med, mn, _ = _time_calls(torch, lambda: dst.copy_(src), 9)
+    del src, dst
+    torch.cuda.empty_cache()
+    rec = {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+           "memory_gib": round(p.total_memory / 2 ** 30, 1),
+           "copy_1gib": {"ms_median": med, "gbs_read_plus_write": 2 * 2 ** 30 / (med * 1e-3) / 1e9,
+                         "frac_of_hbm_peak": 2 * 2 ** 30 / (med * 1e-3) / 1e9 / PEAK_HBM_GBS},
+           "peaks": {"bf16_mfma_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS}}
+    for attr in ("clock_rate", "L2_cache_size"):
+        if hasattr(p, attr):
+            rec[attr] = getattr(p, attr)
+    return rec
 
 
 def _mfma_roofline(flops: float, ms: float, kernel: str, traffic_key=None):
@@ -664,6 +688,7 @@ def main():
            "config": {"workload": "varlen_fp8: fused CSA (m=4) + fused HCA (m'=128) over 32 packed sequences, "
                                   f"T={T}, d={d}, c={c}, fp8 E4M3 entries + per-entry fp32 scales",
                       "tokens": T, "seq_lengths": "U[4096,65536] step 128"}}
+    out["device"] = device_record(torch, dev)
     need_varlen = any(x in legs for x in ("step", "indexer_keys", "decode_append", "rope_store"))
     if need_varlen:
         common = dict(seed=0, in_dtype="bf16", bias_std=cfg["bias_std"], device=dev,

@@ -97,6 +97,12 @@ def _to_device(a, dtype, device):
         if hit is not None:
             _DEV_COPIES.move_to_end(key)
             return hit
+    if torch.cuda.is_current_stream_capturing():
+        # a copy captured into a graph would re-read a temporary pinned
+        # buffer on every replay
+        raise RuntimeError("host metadata (sequence offsets, visible counts) cannot be copied to the device during "
+                           "graph capture: make the same call once on the capturing stream before capturing, so "
+                           "that its device copy is kept")
     d = t.pin_memory().to(device, non_blocking=True)
     if key is not None:
         _DEV_COPIES[key] = d
