@@ -3,9 +3,11 @@
 // The projection ("序列压缩注意力", eq. attn-seqcomp-csa-proj) is the one
 // dense contraction of the compressor: Y = H Wt^T with K = d.  One workgroup
 // computes a 256 x 256 tile of Y with 4 wavefronts (2 x 2, each 128 x 128 as
-// 4 x 4 v_mfma_f32_32x32x16_bf16 accumulators in registers: with one wave per
-// SIMD that instruction sustains ~94% of the bf16 peak on gfx950, the 16x16x32
-// form only ~56%, as measured with back-to-back independent MFMAs).  K advances in
+// 4 x 4 v_mfma_f32_32x32x16_bf16 accumulators in registers).  Under sustained
+// load the chip's power limit sets the rate: a kernel built the same way on
+// v_mfma_f32_16x16x32_bf16 (8 waves of 128 x 64, two per SIMD) drew less
+// power per MFMA and ran at a higher clock, but its matrix cores were
+// correspondingly less busy, and it measured the same throughput.  K advances in
 // 128-byte slabs (64 bf16 / 32 fp32 of every tile row: whole cache lines, so
 // every L2 request is a full line) that are copied global -> LDS directly
 // (global_load_lds_dwordx4, no register staging).  The LDS holds a ring of

@@ -269,3 +269,44 @@ def test_varlen_fp8_config_every_round_and_xcd(gpu_device):
         assert rel.max() <= 2e-2 and rel.max() <= BF16_OBSERVED
         del case, q, s, f32
         torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("mode,out_dtype", [("csa", "f32"), ("csa", "fp8"), ("hca", "bf16"), ("hca", "fp8")])
+def test_sequence_results_independent_of_packing(gpu_device, mode, out_dtype):
+    """No kernel communicates between workgroups (the CSA halo is merged by a
+    separate launch), so the order in which the persistent grid visits tiles
+    cannot change a result.  Tiles never cross sequences, so sequence A is cut
+    into the same tiles whether it is packed alone or after other sequences,
+    which moves its tiles to other workgroups, XCDs and rounds: its entries
+    (and fp8 scales) must be identical bit for bit, and the pooling call's
+    too."""
+    m = 4 if mode == "csa" else 128
+    d, c = 256, 128
+    la = 3000 if mode == "csa" else 6400
+    lengths_alone, lengths_packed = [la], [1000, 777, 1536, la, 300]
+    cases = [synth.compressor_case(mode, L, d, c, m, seed=70, in_dtype="bf16", bias_std=0.3, device=gpu_device)
+             for L in (lengths_alone, lengths_packed)]
+    A_rows = slice(sum(lengths_packed[:3]), sum(lengths_packed[:4]))
+    # the packed case's sequence A gets the alone case's rows and weights
+    packed = cases[1]
+    packed.H[A_rows] = cases[0].H
+    packed.Wt_cat.copy_(cases[0].Wt_cat)
+    for k in packed.biases:
+        packed.biases[k].copy_(cases[0].biases[k])
+    alone_out, alone_scale = _run(cases[0], out_dtype)
+    packed_out, packed_scale = _run(packed, out_dtype)
+    e0 = sum(L // m for L in lengths_packed[:3])
+    E = la // m
+    assert torch.equal(packed_out[e0:e0 + E], alone_out)
+    if out_dtype == "fp8":
+        assert torch.equal(packed_scale[e0:e0 + E], alone_scale)
+    # the pooling call on the projected streams, same check
+    Ys = [sc.project(cs.H, cs.Wt_cat, "bf16") for cs in (cases[0], packed)]
+    b = cases[0].biases
+    if mode == "csa":
+        pools = [sc.pool_csa(Y[:, :c], Y[:, c:2 * c], Y[:, 2 * c:3 * c], Y[:, 3 * c:], b["Ba"], b["Bb"], m, cs.cu_seqlens,
+                             "bf16")[0] for Y, cs in zip(Ys, (cases[0], packed))]
+    else:
+        pools = [sc.pool_hca(Y[:, :c], Y[:, c:], b["B"], m, cs.cu_seqlens, "bf16")[0]
+                 for Y, cs in zip(Ys, (cases[0], packed))]
+    assert torch.equal(pools[1][e0:e0 + E], pools[0])
