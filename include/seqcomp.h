@@ -128,7 +128,7 @@ int seqcomp_project(const void* H, int64_t T, int64_t d, int in_dtype,
  * eq. attn-seqcomp-csa-pool, eq. attn-seqcomp-overlap-bound).
  *   Ca, Cb, Za, Zb: [T x ld_in] of in_dtype, T = cu[batch]; they may be
  *   column slices of one seqcomp_project output.  Ba, Bb: [m x c] fp32.
- *   1 <= m <= 16.  out: [E x c] of out_dtype; out_scale: [E] fp32, required
+ *   c <= ld_in <= 2^32.  1 <= m <= 16.  out: [E x c] of out_dtype; out_scale: [E] fp32, required
  *   iff out_dtype is SEQCOMP_FP8_E4M3 (else ignored, may be NULL).
  *   workspace: seqcomp_workspace_bytes(SEQCOMP_OP_POOL_CSA, ...) bytes.
  */
@@ -244,7 +244,7 @@ size_t seqcomp_append_workspace_bytes(int64_t nb, int64_t c, int out_dtype);
  *   adjacent pairs: pair k (columns c - r + 2k, c - r + 2k + 1) by the angle
  *   pos * rope_base^(-2k / r); the first c - r dimensions are left as they are.
  *   Entry e goes to cache row slots_dev[e] (int64 [E]; NULL: row e); rows
- *   must be distinct; a row outside [0, n_slots) is not stored.
+ *   must be distinct; a row outside [0, n_slots) is not stored; n_slots <= 2^40.
  *   cache_nope  [n_slots x (c - r)] OCP E4M3 codes of the first c - r
  *               dimensions divided by cache_scale[row];
  *   cache_scale [n_slots] fp32: max |x| over those c - r dimensions / 448 (1 if

@@ -171,7 +171,7 @@ int pool_common(bool csa, const void* const* streams, int n_streams, int64_t ld_
   if (!valid_out_dtype(out_dtype)) return SEQCOMP_E_DTYPE;
   if (m < 1 || m > (csa ? kPoolCsaMaxM : kPoolHcaMaxM)) return SEQCOMP_E_UNSUPPORTED;
   if (c < 16 || c % 16 != 0 || c > (int64_t(1) << 20)) return SEQCOMP_E_UNSUPPORTED;
-  if (ld_in < c) return SEQCOMP_E_SHAPE;
+  if (ld_in < c || ld_in > (int64_t(1) << 32)) return SEQCOMP_E_SHAPE;   // row offsets and byte ranges in int64
   const int es = elt_size(in_dtype);
   if ((ld_in * es) % 16 != 0) return SEQCOMP_E_ALIGN;
   int64_t T = 0;
@@ -478,7 +478,7 @@ int seqcomp_rope_store(const void* entries, int in_dtype, int64_t c, int64_t m, 
   int st = check_cu(cu_seqlens_host, batch, &T);
   if (st) return st;
   const int64_t E = entries_of(cu_seqlens_host, batch, m);
-  if (n_slots < 0 || (!slots_dev && n_slots < E)) return SEQCOMP_E_SHAPE;
+  if (n_slots < 0 || n_slots > (int64_t(1) << 40) || (!slots_dev && n_slots < E)) return SEQCOMP_E_SHAPE;
   if (E == 0) return SEQCOMP_OK;
   const int64_t cn = c - rope_dims;
   if (!entries || !cu_seqlens_dev || !cache_scale || (cn > 0 && !cache_nope) || (rope_dims > 0 && !cache_rope))

@@ -117,6 +117,7 @@ def fused(lib, **kw):
     (dict(Za=C_ + 2), "SEQCOMP_E_ALIGN"),
     (dict(ld=516), "SEQCOMP_E_ALIGN"),
     (dict(ld=256), "SEQCOMP_E_SHAPE"),
+    (dict(ld=(1 << 32) + 8), "SEQCOMP_E_SHAPE"),             # row offsets of T rows would overflow
     (dict(cu=_cu(1, 8192)), "SEQCOMP_E_SEQLENS"),
     (dict(cu=_cu(0, 100, 50)), "SEQCOMP_E_SEQLENS"),
     (dict(m=0), "SEQCOMP_E_UNSUPPORTED"),
@@ -269,6 +270,7 @@ def test_rope_store_workspace(lib):
     (dict(base=0.0), "SEQCOMP_E_SHAPE"),
     (dict(base=float("nan")), "SEQCOMP_E_SHAPE"),
     (dict(n_slots=100), "SEQCOMP_E_SHAPE"),                 # no slot map: one row per entry needed
+    (dict(n_slots=(1 << 40) + 1), "SEQCOMP_E_SHAPE"),      # cache byte ranges would overflow
     (dict(cu=_cu(0, -4)), "SEQCOMP_E_SEQLENS"),
     (dict(ent=0), "SEQCOMP_E_NULL"),
     (dict(scale=0), "SEQCOMP_E_NULL"),
