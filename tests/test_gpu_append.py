@@ -64,6 +64,7 @@ def _append_all(case, out_dtype, in_place):
 @pytest.mark.parametrize("lengths,c", [
     ([8, 4, 13, 40, 0, 3, 24], 80),                 # ragged block counts, tails, empty and short sequences
     ([4 * 3] * 70, 64),                              # 70 sequences: two tiles of 64 blocks per call
+    ([8, 12, 4, 20], 1024),                         # c = 1024: 32 channel tiles of the small-batch form
 ])
 def test_append_fp32_matches_whole_sequence(gpu_device, lengths, c):
     case = synth.compressor_case("csa", lengths, 128, c, 4, seed=3, in_dtype="f32", bias_std=0.3, device=gpu_device)

@@ -149,6 +149,25 @@ def test_fused_bf16_operands_multitile(gpu_device, mode, lengths, d, c):
     assert err <= 2e-5
 
 
+@pytest.mark.parametrize("mode,lengths", [("csa", [517, 260]), ("hca", [640, 300])])
+def test_fused_wide_and_deep(gpu_device, mode, lengths):
+    """c = 2048 channels (CSA: 32 N tiles; HCA: 16 channel slices of 128) and
+    d = 8192 (128 K slabs), bf16 operands, fp32 entries.  Each projected
+    value sums 8192 exact bf16 products in fp32; with unit-variance values
+    the accumulation errs by ~2^-24 * sqrt(8192) ~ 5e-6 (observed 3-5e-6),
+    so max abs <= 5e-5 holds with a tenfold margin while a slip in the bias or block bookkeeping (bias
+    std 0.5) moves entries by ~0.1."""
+    m = 4 if mode == "csa" else 128
+    case = synth.compressor_case(mode, lengths, 8192, 2048, m, seed=9, in_dtype="bf16", bias_std=0.5,
+                                 device=gpu_device)
+    out, _ = _run(case, "f32")
+    ref = _oracle_full(case)
+    assert out.shape == ref.shape
+    err = max_abs_err(to64(out), ref)
+    print(f"{mode} c=2048 d=8192: max abs err {err:.3e}")
+    assert err <= 5e-5
+
+
 @pytest.mark.parametrize("T,d,n_out", [(300, 128, 96), (513, 320, 272), (64, 64, 512)])
 def test_project_bf16_operands_f32_out(gpu_device, T, d, n_out):
     """bf16 projection with fp32 output against the float64 product of the same

@@ -44,6 +44,7 @@ def _dev(case, device):
     ([997], 64, 3, 5),                            # m that does not divide the tile
     ([2048 + 7], 512, 16, 256),                   # c = 512, larger m
     ([1500], 192, 4, 96),                         # c = 192: several HCA channel slices, m = 96
+    ([700, 9, 300], 2048, 4, 128),                # c = 2048: four CSA slices of 512, 32 HCA slices
 ])
 def test_pool_fp32_exact(gpu_device, lengths, c, m_csa, m_hca):
     """fp32 streams, fp32 output: max abs error <= 1e-5 against the oracle."""
