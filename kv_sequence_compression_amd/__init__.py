@@ -76,6 +76,7 @@ def _in_code(t: torch.Tensor) -> int:
 
 _DEV_COPIES = collections.OrderedDict()   # (device, stream, dtype, bytes) -> read-only device tensor
 _DEV_COPIES_MAX = 64
+_DEV_COPIES_HELD = {}   # copies that a captured graph reads: kept, whatever the cache evicts
 _DEV_COPY_MAX_BYTES = 1 << 16
 
 
@@ -96,6 +97,10 @@ def _to_device(a, dtype, device):
         hit = _DEV_COPIES.get(key)
         if hit is not None:
             _DEV_COPIES.move_to_end(key)
+            if torch.cuda.is_current_stream_capturing():
+                # the graph keeps this address for every replay: freeing the
+                # copy on eviction would let the allocator hand it out again
+                _DEV_COPIES_HELD[key] = hit
             return hit
     if torch.cuda.is_current_stream_capturing():
         # a copy captured into a graph would re-read a temporary pinned

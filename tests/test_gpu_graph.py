@@ -5,6 +5,10 @@ result bit for bit (the same kernels on the same inputs).  The library
 launches kernels only -- no copies, fills or allocations inside a call -- so
 a captured call replays as it ran."""
 
+import gc
+import weakref
+
+import numpy as np
 import pytest
 import torch
 
@@ -87,3 +91,33 @@ def test_capture_refuses_an_uncached_host_copy(gpu_device):
         with torch.cuda.graph(g, stream=s):
             sc.compress_fused("hca", case.H, case.Wt_cat, case.biases["B"], None, 128, [0, 1024 - 128, 1024],
                               "bf16")
+
+
+def test_captured_offsets_outlive_cache_eviction(gpu_device):
+    """The device copy of the offsets that a captured call reads stays
+    allocated after the binding's cache has evicted it (more than its 64
+    layouts seen since), so the allocator cannot hand that memory to another
+    tensor; replays after the flood still equal the eager result.  The copy's
+    survival is checked before any replay."""
+    case = synth.compressor_case("csa", [900, 260], 128, 64, 4, seed=53, in_dtype="bf16", bias_std=0.3,
+                                 device=gpu_device)
+    b = case.biases
+    s = torch.cuda.Stream(gpu_device)
+    with torch.cuda.stream(s):
+        ref, _ = sc.compress_fused("csa", case.H, case.Wt_cat, b["Ba"], b["Bb"], 4, case.cu_seqlens, "bf16")
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        out, _ = sc.compress_fused("csa", case.H, case.Wt_cat, b["Ba"], b["Bb"], 4, case.cu_seqlens, "bf16")
+    host = np.ascontiguousarray(np.asarray(case.cu_seqlens, dtype=np.int64))
+    with torch.cuda.stream(s):
+        captured = weakref.ref(sc._to_device(host, torch.int64, gpu_device))   # the cached copy the graph reads
+        for k in range(100):                                                   # evict it from the cache
+            sc._to_device(np.array([0, 4 * (k + 1), 4 * (k + 2)], dtype=np.int64), torch.int64, gpu_device)
+    s.synchronize()
+    gc.collect()
+    assert captured() is not None, "the captured offsets' device copy was freed"
+
+    def check(i):
+        assert torch.equal(out, ref), f"replay {i}"
+    _replays(g, check)
