@@ -14,9 +14,17 @@ Functions (each returns torch tensors on the inputs' device):
 * ``csa_append(H, Wt, Ba, Bb, state, out_dtype, state_out)`` -> (entries, scale|None, state)
 * ``csa_empty_state(nb, c, device)``                   -> the state of sequences with no block yet
 * ``rope_store(entries, m, cu_seqlens, cache, ...)``     partial RoPE + bf16/fp8 store into a cache
+* ``indexer_topk(q, w, keys, k, ...)``                   -> (indices, scores|None) of the k best keys
+* ``shared_kv_mqa(q, kv, ...)``                          -> (out, lse|None), dense attention with a sink
 
 ``out_dtype`` is one of "f32", "bf16", "fp8" (OCP E4M3FN codes stored as
 uint8 with one fp32 scale per entry).
+
+Every tensor argument is checked before the call: its dtype, its shape (the
+sizes the kernels will read), a dense layout, and the device of the first
+input.  The kernels take raw pointers, so a host tensor, a short buffer or a
+strided view would otherwise be read out of place.  Sequence offsets may not
+reach past the rows given.
 """
 
 from __future__ import annotations
@@ -30,8 +38,8 @@ import torch
 from . import _lib
 
 __all__ = ["SeqcompError", "project", "pool_csa", "pool_hca", "compress_fused", "compress_fused_noalloc",
-           "csa_append", "csa_empty_state",
-           "rope_store", "rope_cache", "num_entries", "workspace_bytes", "version", "lib"]
+           "csa_append", "csa_empty_state", "rope_store", "rope_cache", "indexer_topk", "shared_kv_mqa",
+           "num_entries", "workspace_bytes", "version", "lib"]
 
 _DT_CODE = {"f32": _lib.F32, "bf16": _lib.BF16, "fp8": _lib.FP8_E4M3}
 _TORCH_IN = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16}
@@ -66,6 +74,45 @@ def _stream(dev: torch.device):
 
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need(t, name: str, dtypes, shape=None, dense: bool = True):
+    """Check one tensor argument's dtype, shape and layout (its device is
+    checked with the others' by _one_gpu)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not supported ({', '.join(str(d) for d in dtypes)})")
+    if shape is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(int(x) for x in shape)}, not {tuple(t.shape)}")
+    if dense and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _one_gpu(**tensors) -> torch.device:
+    """All given tensors (None entries skipped) on one GPU; returns it."""
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a GPU, not {t.device}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other inputs on {dev}")
+    return dev
+
+
+def _need_rows(host: np.ndarray, rows: int, name: str):
+    """Offsets must reach no further than the rows the caller passed."""
+    if host.size >= 1 and host[-1] > rows:
+        raise ValueError(f"{name} reaches row {int(host[-1])}, past the {rows} rows given")
+
+
+_IN = (torch.float32, torch.bfloat16)
+_F32 = (torch.float32,)
+_BF16 = (torch.bfloat16,)
 
 
 def _in_code(t: torch.Tensor) -> int:
@@ -162,8 +209,15 @@ def project(H: torch.Tensor, Wt: torch.Tensor, out_dtype: str = "bf16", out: tor
     `out`, if given, is a [T x n_out] view with unit column stride and any row
     stride >= n_out (e.g. the left columns of a wider buffer); it is written
     in place and returned."""
+    _need(H, "H", _IN)
+    if H.dim() != 2:
+        raise ValueError("H must be [T x d]")
     T, d = H.shape
-    n_out = Wt.shape[0]
+    n_out = Wt.shape[0] if isinstance(Wt, torch.Tensor) and Wt.dim() == 2 else -1
+    _need(Wt, "Wt", (H.dtype,), (n_out, d))
+    if out is not None:
+        _need(out, "out", (_TORCH_OUT[out_dtype],), (T, n_out), dense=False)
+    _one_gpu(H=H, Wt=Wt, out=out)
     if out is None:
         Y = torch.empty((T, n_out), dtype=_TORCH_OUT[out_dtype], device=H.device)
     else:
@@ -175,20 +229,24 @@ def project(H: torch.Tensor, Wt: torch.Tensor, out_dtype: str = "bf16", out: tor
     return Y
 
 
-def _pool_args(x: torch.Tensor):
+def _pool_args(x, name: str, like=None):
+    _need(x, name, _IN if like is None else (like.dtype,), None if like is None else like.shape, dense=False)
     if x.dim() != 2 or x.stride(1) != 1:
-        raise ValueError("pooling streams must be 2-D with unit channel stride")
+        raise ValueError(f"{name}: pooling streams must be 2-D with unit channel stride")
     return x.stride(0)
 
 
 def pool_csa(Ca, Cb, Za, Zb, Ba, Bb, m: int, cu_seqlens=None, out_dtype: str = "bf16"):
     """CSA pooling of materialised streams; returns (entries [E x c], scale [E] or None)."""
-    ld = _pool_args(Ca)
-    if any(_pool_args(x) != ld for x in (Cb, Za, Zb)):
+    ld = _pool_args(Ca, "Ca")
+    if any(_pool_args(x, n, Ca) != ld for x, n in ((Cb, "Cb"), (Za, "Za"), (Zb, "Zb"))):
         raise ValueError("the four streams must share one row stride")
     c = Ca.shape[1]
-    dev = Ca.device
+    _need(Ba, "Ba", _F32, (m, c))
+    _need(Bb, "Bb", _F32, (m, c))
+    dev = _one_gpu(Ca=Ca, Cb=Cb, Za=Za, Zb=Zb, Ba=Ba, Bb=Bb)
     host, cu_dev = _cu_arrays([0, Ca.shape[0]] if cu_seqlens is None else cu_seqlens, dev)
+    _need_rows(host, Ca.shape[0], "cu_seqlens")
     E = num_entries(host, m)
     out, scale = _alloc_out(E, c, out_dtype, dev)
     ws_n = workspace_bytes(_lib.OP_POOL_CSA, 0, m, c, host, out_dtype)
@@ -202,12 +260,14 @@ def pool_csa(Ca, Cb, Za, Zb, Ba, Bb, m: int, cu_seqlens=None, out_dtype: str = "
 
 def pool_hca(C, Z, B, m: int, cu_seqlens=None, out_dtype: str = "bf16"):
     """HCA pooling of materialised streams; returns (entries [E x c], scale [E] or None)."""
-    ld = _pool_args(C)
-    if _pool_args(Z) != ld:
+    ld = _pool_args(C, "C")
+    if _pool_args(Z, "Z", C) != ld:
         raise ValueError("C and Z must share one row stride")
     c = C.shape[1]
-    dev = C.device
+    _need(B, "B", _F32, (m, c))
+    dev = _one_gpu(C=C, Z=Z, B=B)
     host, cu_dev = _cu_arrays([0, C.shape[0]] if cu_seqlens is None else cu_seqlens, dev)
+    _need_rows(host, C.shape[0], "cu_seqlens")
     E = num_entries(host, m)
     out, scale = _alloc_out(E, c, out_dtype, dev)
     ws_n = workspace_bytes(_lib.OP_POOL_HCA, 0, m, c, host, out_dtype)
@@ -218,16 +278,34 @@ def pool_hca(C, Z, B, m: int, cu_seqlens=None, out_dtype: str = "bf16"):
     return out, scale
 
 
-def compress_fused(mode: str, H, Wt, Ba, Bb, m: int, cu_seqlens=None, out_dtype: str = "bf16"):
-    """Fused projection + pooling (mode "csa" with m=4, or "hca" with m=128)."""
-    mcode = {"csa": _lib.MODE_CSA, "hca": _lib.MODE_HCA}[mode]
+def _fused_args(mode: str, H, Wt, Ba, Bb, m: int):
+    """Checks shared by both fused entry points; returns (mode code, T, d, c)."""
+    if mode not in ("csa", "hca"):
+        raise ValueError('mode must be "csa" or "hca"')
+    _need(H, "H", _IN)
+    if H.dim() != 2:
+        raise ValueError("H must be [T x d]")
     T, d = H.shape
     S = 4 if mode == "csa" else 2
-    c = Wt.shape[0] // S
-    if Wt.shape != (S * c, d):
-        raise ValueError(f"Wt must be [{S}*c x d]")
+    c = Wt.shape[0] // S if isinstance(Wt, torch.Tensor) and Wt.dim() == 2 else 0
+    _need(Wt, f"Wt ([{S}*c x d])", (H.dtype,), (S * c, d))
+    if mode == "csa":
+        _need(Ba, "Ba", _F32, (m, c))
+        _need(Bb, "Bb", _F32, (m, c))
+    else:
+        _need(Ba, "B", _F32, (m, c))
+        if Bb is not None:
+            raise ValueError("HCA takes one bias: Bb must be None")
+    _one_gpu(H=H, Wt=Wt, Ba=Ba, Bb=Bb)
+    return {"csa": _lib.MODE_CSA, "hca": _lib.MODE_HCA}[mode], T, d, c
+
+
+def compress_fused(mode: str, H, Wt, Ba, Bb, m: int, cu_seqlens=None, out_dtype: str = "bf16"):
+    """Fused projection + pooling (mode "csa" with m=4, or "hca" with m=128)."""
+    mcode, T, d, c = _fused_args(mode, H, Wt, Ba, Bb, m)
     dev = H.device
     host, cu_dev = _cu_arrays([0, T] if cu_seqlens is None else cu_seqlens, dev)
+    _need_rows(host, T, "cu_seqlens")
     E = num_entries(host, m)
     out, scale = _alloc_out(E, c, out_dtype, dev)
     ws_n = workspace_bytes(_lib.OP_FUSED, mcode, m, c, host, out_dtype)
@@ -245,19 +323,18 @@ def compress_fused_noalloc(mode: str, H, Wt, Ba, Bb, m: int, cu_seqlens=None, ou
     uses its own per-device scratch (64 MiB) instead of a workspace.  `out`
     (and `out_scale` for fp8) may be passed pre-allocated; otherwise they are
     allocated here, outside the library call."""
-    mcode = {"csa": _lib.MODE_CSA, "hca": _lib.MODE_HCA}[mode]
-    T, d = H.shape
-    S = 4 if mode == "csa" else 2
-    c = Wt.shape[0] // S
-    if Wt.shape != (S * c, d):
-        raise ValueError(f"Wt must be [{S}*c x d]")
+    mcode, T, d, c = _fused_args(mode, H, Wt, Ba, Bb, m)
     dev = H.device
     host, cu_dev = _cu_arrays([0, T] if cu_seqlens is None else cu_seqlens, dev)
+    _need_rows(host, T, "cu_seqlens")
     E = num_entries(host, m)
     if out is None:
         out, out_scale = _alloc_out(E, c, out_dtype, dev)
-    elif out.shape != (E, c) or out.dtype != _TORCH_OUT[out_dtype] or not out.is_contiguous():
-        raise ValueError(f"out must be a contiguous [{E} x {c}] {_TORCH_OUT[out_dtype]} tensor")
+    else:
+        _need(out, "out", (_TORCH_OUT[out_dtype],), (E, c))
+        if out_dtype == "fp8":
+            _need(out_scale, "out_scale", _F32, (E,))
+        _one_gpu(H=H, out=out, out_scale=out_scale if out_dtype == "fp8" else None)
     _check(lib().seqcomp_compress_fused_noalloc(mcode, int(m), _ptr(H), d, _in_code(H), _ptr(Wt), c, _ptr(Ba),
                                                 _ptr(Bb), _i64p(host), _ptr(cu_dev), host.size - 1, _ptr(out),
                                                 _DT_CODE[out_dtype], _ptr(out_scale), _stream(dev)),
@@ -278,18 +355,24 @@ def csa_append(H, Wt, Ba, Bb, state=None, out_dtype: str = "bf16", state_out=Non
     state_out [nb, 3, c]).  `state` is what the previous call returned for
     these sequences (None: every sequence starts here).  Passing
     state_out=state updates the state in place."""
+    _need(H, "H", _IN)
+    if H.dim() != 2:
+        raise ValueError("H must be [4 nb x d]")
     T, d = H.shape
     if T % 4 != 0:
         raise ValueError("H must hold whole blocks of 4 rows")
     nb = T // 4
-    c = Wt.shape[0] // 4
-    if Wt.shape != (4 * c, d):
-        raise ValueError("Wt must be [4*c x d]")
-    dev = H.device
+    c = Wt.shape[0] // 4 if isinstance(Wt, torch.Tensor) and Wt.dim() == 2 else 0
+    _need(Wt, "Wt ([4*c x d])", (H.dtype,), (4 * c, d))
+    _need(Ba, "Ba", _F32, (4, c))
+    _need(Bb, "Bb", _F32, (4, c))
+    if state is not None:
+        _need(state, "state", _F32, (nb, 3, c))
+    if state_out is not None:
+        _need(state_out, "state_out", _F32, (nb, 3, c))
+    dev = _one_gpu(H=H, Wt=Wt, Ba=Ba, Bb=Bb, state=state, state_out=state_out)
     if state is None:
         state = csa_empty_state(nb, c, dev)
-    if state.shape != (nb, 3, c) or state.dtype != torch.float32 or not state.is_contiguous():
-        raise ValueError(f"state must be a contiguous float32 [{nb}, 3, {c}] tensor")
     if state_out is None:
         state_out = torch.empty_like(state)
     out, scale = _alloc_out(nb, c, out_dtype, dev)
@@ -314,15 +397,25 @@ def rope_store(entries, m: int, cu_seqlens, cache, rope_dims: int = 64, rope_bas
     """Partial RoPE on the last `rope_dims` dimensions of every packed entry
     (position: its block centre plus pos0 of its sequence) and the store into
     `cache` = (nope, scale, rope) at rows `slots` (default: row e for entry e)."""
+    _need(entries, "entries", _IN)
+    if entries.dim() != 2:
+        raise ValueError("entries must be [E x c]")
     E, c = entries.shape
-    dev = entries.device
-    host, cu_dev = _cu_arrays(cu_seqlens, dev)
     nope, scale, rope = cache
-    n_slots = scale.shape[0]
-    if nope.shape != (n_slots, c - rope_dims) or rope.shape != (n_slots, rope_dims):
-        raise ValueError("cache shapes do not match c and rope_dims")
+    _need(scale, "cache scale", _F32)
+    n_slots = scale.shape[0] if scale.dim() == 1 else -1
+    _need(nope, "cache nope", (torch.uint8,), (n_slots, c - rope_dims))
+    _need(rope, "cache rope", _BF16, (n_slots, rope_dims))
+    dev = _one_gpu(entries=entries, nope=nope, scale=scale, rope=rope)
+    host, cu_dev = _cu_arrays(cu_seqlens, dev)
+    if num_entries(host, m) != E:
+        raise ValueError(f"cu_seqlens and m give {num_entries(host, m)} entries, entries holds {E}")
     p0 = None if pos0 is None else _to_device(pos0, torch.int64, dev)
     sl = None if slots is None else _to_device(slots, torch.int64, dev)
+    if p0 is not None and p0.numel() != host.size - 1:
+        raise ValueError("pos0 must hold one position per sequence")
+    if sl is not None and sl.numel() != E:
+        raise ValueError("slots must hold one cache row per entry")
     ws_n = lib().seqcomp_rope_store_workspace_bytes(int(m), _i64p(host), host.size - 1)
     ws = _alloc_ws(ws_n, dev)
     _check(lib().seqcomp_rope_store(_ptr(entries), _in_code(entries), c, int(m), _i64p(host), _ptr(cu_dev),
@@ -340,16 +433,25 @@ def indexer_topk(q, w, keys, k: int, cu_q=None, cu_k=None, n_valid=None, with_sc
     bf16; cu_q / cu_k pack queries and keys by sequence (default: one
     sequence); n_valid [T] int32: keys visible to each query (default: all).
     Returns (idx int32 [T x k], scores fp32 [T x k] or None)."""
-    T = q.shape[0]
+    _need(q, "q", _BF16)
+    if q.dim() != 3:
+        raise ValueError("q must be [T x H x D]")
+    T, Hh, D = q.shape
+    _need(w, "w", _F32, (T, Hh))
+    _need(keys, "keys", _BF16)
+    if keys.dim() != 2 or keys.shape[1] != D:
+        raise ValueError("keys must be [N x D]")
     N = keys.shape[0]
-    dev = q.device
-    if q.dim() != 3 or keys.dim() != 2 or w.shape != (T, q.shape[1]):
-        raise ValueError("q must be [T x H x D], w [T x H], keys [N x D]")
+    dev = _one_gpu(q=q, w=w, keys=keys)
     hq, cq = _cu_arrays([0, T] if cu_q is None else cu_q, dev)
     hk, ck = _cu_arrays([0, N] if cu_k is None else cu_k, dev)
     if hq.size != hk.size:
         raise ValueError("cu_q and cu_k must describe the same number of sequences")
+    _need_rows(hq, T, "cu_q")
+    _need_rows(hk, N, "cu_k")
     nv = None if n_valid is None else _to_device(n_valid, torch.int32, dev)
+    if nv is not None and nv.numel() < (int(hq[-1]) if hq.size else 0):
+        raise ValueError("n_valid must hold one count per query")
     idx = torch.empty((T, int(k)), dtype=torch.int32, device=dev)
     sc = torch.empty((T, int(k)), dtype=torch.float32, device=dev) if with_scores else None
     ws_n = lib().seqcomp_indexer_workspace_bytes(_i64p(hq), hq.size - 1)
@@ -372,16 +474,28 @@ def shared_kv_mqa(q, kv, cu_q=None, cu_k=None, n_valid=None, k_sink=None, v_sink
     sequence (default: one sequence); n_valid [T] int32 (default: all);
     k_sink / v_sink [512] bf16 or None; scale defaults to 1/sqrt(512).
     Returns (out [T x 128 x 512] of out_dtype, lse [T x 128] fp32 or None)."""
-    T = q.shape[0]
+    _need(q, "q", _BF16)
+    if q.dim() != 3:
+        raise ValueError("q must be [T x H x D]")
+    T, _, D = q.shape
+    _need(kv, "kv", _BF16)
+    if kv.dim() != 2 or kv.shape[1] != D:
+        raise ValueError("kv must be [N x D]")
     N = kv.shape[0]
-    dev = q.device
-    if q.dim() != 3 or kv.dim() != 2:
-        raise ValueError("q must be [T x H x D] and kv [N x D]")
+    if k_sink is not None:
+        _need(k_sink, "k_sink", _BF16, (D,))
+    if v_sink is not None:
+        _need(v_sink, "v_sink", _BF16, (D,))
+    dev = _one_gpu(q=q, kv=kv, k_sink=k_sink, v_sink=v_sink)
     hq, cq = _cu_arrays([0, T] if cu_q is None else cu_q, dev)
     hk, ck = _cu_arrays([0, N] if cu_k is None else cu_k, dev)
     if hq.size != hk.size:
         raise ValueError("cu_q and cu_k must describe the same number of sequences")
+    _need_rows(hq, T, "cu_q")
+    _need_rows(hk, N, "cu_k")
     nv = None if n_valid is None else _to_device(n_valid, torch.int32, dev)
+    if nv is not None and nv.numel() < (int(hq[-1]) if hq.size else 0):
+        raise ValueError("n_valid must hold one count per query")
     sc_ = float(scale) if scale is not None else 1.0 / float(np.sqrt(q.shape[2]))
     out = torch.empty(tuple(q.shape), dtype=_TORCH_OUT[out_dtype], device=dev)
     lse = torch.empty((T, q.shape[1]), dtype=torch.float32, device=dev) if with_lse else None
