@@ -292,10 +292,21 @@ int fused_impl(int mode, int64_t m, const void* H, int64_t d, int in_dtype, cons
   const bool fp8 = out_dtype == SEQCOMP_FP8_E4M3;
   void* dst = fp8 ? (void*)(wsb + L.stage_off) : out;
   const int dst_dt = fp8 ? DT_F32 : out_dtype;
-  hipError_t e = launch_plan(cu_seqlens_dev, (int)batch, (int)m, kFusedTileRows, tiles, (int)L.n_tiles, s);
+  // Calls of at most two rounds of the persistent grid over few sequences:
+  // the kernels look their tiles up from the offsets and the planner launch
+  // goes (the 8192-token CSA call: 178 -> 175 us).  Longer calls keep the
+  // planner's table, one load per tile instead of a lookup per tile.
+  const int64_t n_nt = csa ? (c + 63) / 64 : (c + 127) / 128;
+  const bool planned = batch > kTileLookupMaxBatch || L.n_tiles * n_nt > 2 * (int64_t)device_cu_count();
+  hipError_t e = planned
+                     ? launch_plan(cu_seqlens_dev, (int)batch, (int)m, kFusedTileRows, tiles, (int)L.n_tiles, s)
+                     : hipSuccess;
+  const TileRec* tt = planned ? tiles : nullptr;
   if (e == hipSuccess)
-    e = launch_fused(mode, in_dtype, dst_dt, H, (int)d, Wt, (int)c, Ba, Bb, tiles, (int)L.n_tiles, dst, halo, s);
-  if (e == hipSuccess && csa) e = launch_csa_fixup(dst_dt, tiles, (int)L.n_tiles, (int)c, halo, dst, s);
+    e = launch_fused(mode, in_dtype, dst_dt, H, (int)d, Wt, (int)c, Ba, Bb, tt, cu_seqlens_dev, (int)batch,
+                     (int)L.n_tiles, dst, halo, s);
+  if (e == hipSuccess && csa)
+    e = launch_csa_fixup(dst_dt, tt, cu_seqlens_dev, (int)batch, (int)L.n_tiles, (int)c, halo, dst, s);
   if (e == hipSuccess && fp8)
     e = launch_quant_fp8(reinterpret_cast<const float*>(dst), E, (int)c, static_cast<uint8_t*>(out), out_scale, s);
   return hip_status(e);

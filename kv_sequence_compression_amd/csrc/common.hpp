@@ -19,6 +19,50 @@ enum : int32_t { TILE_FIRST = 1 };
 // flags bits 1..31: index of the tile's sequence in the packed batch
 __host__ __device__ inline int tile_seq(int32_t flags) { return (int)((uint32_t)flags >> 1); }
 
+// Tile k of a packed batch of at most kTileLookupMaxBatch sequences, the
+// record the planner would write, computed by one wave from the sequence
+// offsets: lane b takes sequence b (floor(L_b / m) entries, their rows cut
+// into tiles of tile_rows), two inclusive scans over the lanes give every
+// sequence's first tile and first entry, and tile k belongs to the first
+// sequence whose tiles end past k.  Every lane of the wave must take part;
+// the result is wave-uniform.  k must be below the batch's tile count.
+constexpr int kTileLookupMaxBatch = 64;
+__device__ __forceinline__ TileRec tile_lookup(const int64_t* __restrict__ cu, int batch, int m, int tile_rows,
+                                               int k) {
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));   // keep the scans inside a caller's persistent loop
+  int row0 = 0, ne = 0;
+  if (lane < batch) {
+    const int64_t start = cu[lane];
+    row0 = (int)start;
+    ne = (int)((cu[lane + 1] - start) / m);
+  }
+  const int nt = (ne * m + tile_rows - 1) / tile_rows;
+  int tend = nt, eend = ne;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int a = __shfl_up(tend, off, 64);
+    const int e = __shfl_up(eend, off, 64);
+    if (lane >= off) {
+      tend += a;
+      eend += e;
+    }
+  }
+  const unsigned long long past = __ballot(tend > k);
+  const int s = past ? __ffsll(past) - 1 : 0;
+  const int t0 = __shfl(tend - nt, s, 64);
+  const int e0 = __shfl(eend - ne, s, 64);
+  const int r0 = __shfl(row0, s, 64);
+  const int rows = __shfl(ne * m, s, 64);
+  const int j = k - t0;
+  TileRec r;
+  r.row_start = __builtin_amdgcn_readfirstlane(r0 + j * tile_rows);
+  r.n_rows = __builtin_amdgcn_readfirstlane(min(tile_rows, rows - j * tile_rows));
+  r.entry_start = __builtin_amdgcn_readfirstlane(e0 + j * (tile_rows / m));
+  r.flags = __builtin_amdgcn_readfirstlane((j == 0 ? TILE_FIRST : 0) | (s << 1));
+  return r;
+}
+
 enum DType : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
 
 // log2(e): exp(x) = 2^(x * log2 e); v_exp_f32 evaluates 2^x.

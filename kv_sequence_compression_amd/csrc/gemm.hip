@@ -94,6 +94,11 @@ struct Args {
   int64_t nb;              // blocks (= entries)
   // grid
   int n_mt, n_nt;
+  // fused kernels built with LOOKUP: tiles found from the sequence offsets
+  // (tile_lookup) instead of the planner's table; batch <= kTileLookupMaxBatch
+  const int64_t* cu;
+  int batch;
+  int m;
 };
 
 template <int DIN>
@@ -669,8 +674,10 @@ __device__ void epilogue_hca(const Args& a, WaveAcc& acc, const TileRec& t, int 
 // One logical tile.  The thread index is passed through an empty asm
 // statement so the compiler cannot hoist lane-derived values out of the
 // persistent loop (they would stay live across the K loop and crowd out the
-// accumulators).
-template <int DIN, int MODE, int DOUT>
+// accumulators).  LOOKUP: the tile record comes from the sequence offsets,
+// not from the planner's table (a separate instantiation, so the kernels
+// that read the table are built exactly as without it).
+template <int DIN, int MODE, int DOUT, bool LOOKUP>
 __device__ __forceinline__ void run_tile(const Args& a, int L, char* lds) {
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
@@ -685,7 +692,7 @@ __device__ __forceinline__ void run_tile(const Args& a, int L, char* lds) {
     row0 = (int64_t)mt * kTile;
     nvalid = (int)min<int64_t>(kTile, a.T - row0);
   } else {
-    t = a.tiles[mt];
+    t = LOOKUP ? tile_lookup(a.cu, a.batch, a.m, kTile, mt) : a.tiles[mt];
     row0 = t.row_start;
     nvalid = t.n_rows;
   }
@@ -714,13 +721,13 @@ __device__ __forceinline__ void run_tile(const Args& a, int L, char* lds) {
 // tiles.  In every round each XCD owns one contiguous range of logical tiles
 // (N fastest), so the workgroups that share an M panel of H start it
 // together and advance through K in step: their H slabs hit in the XCD's L2.
-template <int DIN, int MODE, int DOUT>
+template <int DIN, int MODE, int DOUT, bool LOOKUP = false>
 __global__ __launch_bounds__(kThreads, 1) void tile_kernel(Args a) {
   __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
   const int G = a.n_mt * a.n_nt;
   const int P = gridDim.x;
   for (int L = xcd_remap(blockIdx.x, P); L < G; L += P) {
-    run_tile<DIN, MODE, DOUT>(a, L, lds);
+    run_tile<DIN, MODE, DOUT, LOOKUP>(a, L, lds);
     __syncthreads();   // the epilogue's LDS use ends before the next tile's loads
   }
 }
@@ -728,10 +735,11 @@ __global__ __launch_bounds__(kThreads, 1) void tile_kernel(Args a) {
 // First entry of every tile that continues a sequence: merge the tile's
 // first-block a-partial with the previous tile's last-block b-partial.
 template <int DOUT>
-__global__ __launch_bounds__(256) void csa_fixup_kernel(const TileRec* __restrict__ tiles, int c,
-                                                        const float* __restrict__ halo, char* __restrict__ out) {
+__global__ __launch_bounds__(256) void csa_fixup_kernel(const TileRec* __restrict__ tiles, const int64_t* __restrict__ cu,
+                                                        int batch, int c, const float* __restrict__ halo,
+                                                        char* __restrict__ out) {
   const int tile = blockIdx.x;
-  const TileRec t = tiles[tile];
+  const TileRec t = tiles ? tiles[tile] : tile_lookup(cu, batch, 4, kTile, tile);
   if (t.flags & TILE_FIRST) return;
   const float* ha = halo + (int64_t)tile * 6 * c;
   const float* hb = halo + (int64_t)(tile - 1) * 6 * c;
@@ -1328,21 +1336,21 @@ AppendPlan append_plan(int64_t nb, int c, int nk) {
   return p;
 }
 
-template <int DIN, int MODE, int DOUT>
+template <int DIN, int MODE, int DOUT, bool LOOKUP = false>
 hipError_t launch_tile(const Args& a, hipStream_t stream) {
   const int G = a.n_mt * a.n_nt;
   const int P = min(G, device_cu_count());   // one workgroup of the tile kernels fits per CU
-  hipLaunchKernelGGL((tile_kernel<DIN, MODE, DOUT>), dim3(P), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((tile_kernel<DIN, MODE, DOUT, LOOKUP>), dim3(P), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int MODE>
+template <int MODE, bool LOOKUP = false>
 hipError_t dispatch(int in_dt, int out_dt, const Args& a, hipStream_t stream) {
   if (in_dt == DT_BF16)
-    return out_dt == DT_BF16 ? launch_tile<DT_BF16, MODE, DT_BF16>(a, stream)
-                             : launch_tile<DT_BF16, MODE, DT_F32>(a, stream);
-  return out_dt == DT_BF16 ? launch_tile<DT_F32, MODE, DT_BF16>(a, stream)
-                           : launch_tile<DT_F32, MODE, DT_F32>(a, stream);
+    return out_dt == DT_BF16 ? launch_tile<DT_BF16, MODE, DT_BF16, LOOKUP>(a, stream)
+                             : launch_tile<DT_BF16, MODE, DT_F32, LOOKUP>(a, stream);
+  return out_dt == DT_BF16 ? launch_tile<DT_F32, MODE, DT_BF16, LOOKUP>(a, stream)
+                           : launch_tile<DT_F32, MODE, DT_F32, LOOKUP>(a, stream);
 }
 
 }  // namespace
@@ -1366,8 +1374,8 @@ hipError_t launch_project(int in_dt, int out_dt, const void* H, int64_t T, int d
 }
 
 hipError_t launch_fused(int mode, int in_dt, int out_dt, const void* H, int d, const void* Wt, int c,
-                        const float* Ba, const float* Bb, const TileRec* tiles, int n_tiles, void* out, float* halo,
-                        hipStream_t stream) {
+                        const float* Ba, const float* Bb, const TileRec* tiles, const int64_t* cu_dev, int batch,
+                        int n_tiles, void* out, float* halo, hipStream_t stream) {
   Args a{};
   const int es = in_dt == DT_BF16 ? 2 : 4;
   a.H = static_cast<const char*>(H);
@@ -1378,16 +1386,19 @@ hipError_t launch_fused(int mode, int in_dt, int out_dt, const void* H, int d, c
   a.Ba = Ba;
   a.Bb = Bb;
   a.tiles = tiles;
+  a.cu = cu_dev;
+  a.batch = batch;
+  a.m = mode == 0 ? 4 : 128;
   a.halo = halo;
   a.out = static_cast<char*>(out);
   a.n_mt = n_tiles;
   a.n_out = 1;
   if (mode == 0) {   // CSA: 64 channels x 4 streams per N tile
     a.n_nt = (c + 63) / 64;
-    return dispatch<MODE_CSA>(in_dt, out_dt, a, stream);
+    return tiles ? dispatch<MODE_CSA>(in_dt, out_dt, a, stream) : dispatch<MODE_CSA, true>(in_dt, out_dt, a, stream);
   }
   a.n_nt = (c + 127) / 128;   // HCA: 128 channels x 2 streams per N tile
-  return dispatch<MODE_HCA>(in_dt, out_dt, a, stream);
+  return tiles ? dispatch<MODE_HCA>(in_dt, out_dt, a, stream) : dispatch<MODE_HCA, true>(in_dt, out_dt, a, stream);
 }
 
 size_t append_partial_bytes(int64_t nb, int c) {
@@ -1468,14 +1479,14 @@ hipError_t launch_csa_append(int in_dt, int out_dt, const void* H, int64_t nb, i
   return hipGetLastError();
 }
 
-hipError_t launch_csa_fixup(int out_dt, const TileRec* tiles, int n_tiles, int c, const float* halo, void* out,
-                            hipStream_t stream) {
+hipError_t launch_csa_fixup(int out_dt, const TileRec* tiles, const int64_t* cu_dev, int batch, int n_tiles, int c,
+                            const float* halo, void* out, hipStream_t stream) {
   if (out_dt == DT_BF16)
-    hipLaunchKernelGGL(csa_fixup_kernel<DT_BF16>, dim3(n_tiles), dim3(256), 0, stream, tiles, c, halo,
-                       static_cast<char*>(out));
+    hipLaunchKernelGGL(csa_fixup_kernel<DT_BF16>, dim3(n_tiles), dim3(256), 0, stream, tiles, cu_dev, batch, c,
+                       halo, static_cast<char*>(out));
   else
-    hipLaunchKernelGGL(csa_fixup_kernel<DT_F32>, dim3(n_tiles), dim3(256), 0, stream, tiles, c, halo,
-                       static_cast<char*>(out));
+    hipLaunchKernelGGL(csa_fixup_kernel<DT_F32>, dim3(n_tiles), dim3(256), 0, stream, tiles, cu_dev, batch, c,
+                       halo, static_cast<char*>(out));
   return hipGetLastError();
 }
 

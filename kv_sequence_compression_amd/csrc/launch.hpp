@@ -57,9 +57,12 @@ hipError_t launch_project(int in_dt, int out_dt, const void* H, int64_t T, int d
 // `halo` holds per tile the fp32 (M, S, A) triples of the first block's
 // a-stream and the last block's b-stream (6 * c floats per tile); the fix-up
 // kernel then writes the first entry of every tile that continues a sequence.
+// `tiles` is the planner's table, or NULL for batches of at most
+// kTileLookupMaxBatch sequences: the kernels then find their tiles from
+// cu_dev themselves (tile_lookup), and no planner launch is needed.
 hipError_t launch_fused(int mode, int in_dt, int out_dt, const void* H, int d, const void* Wt, int c,
-                        const float* Ba, const float* Bb, const TileRec* tiles, int n_tiles, void* out,
-                        float* halo, hipStream_t stream);
+                        const float* Ba, const float* Bb, const TileRec* tiles, const int64_t* cu_dev, int batch,
+                        int n_tiles, void* out, float* halo, hipStream_t stream);
 
 // CSA decode append: nb independent blocks of 4 rows of H; entry j merges
 // block j's a-partial with state_in[j] (the previous block's b-partial, fp32
@@ -102,7 +105,7 @@ hipError_t launch_mqa_sink(int out_dt, const void* q, const void* kv, const int6
                            const TileRec* tiles, int T, const void* k_sink, const void* v_sink, float scale, void* out,
                            float* lse, hipStream_t stream);
 
-hipError_t launch_csa_fixup(int out_dt, const TileRec* tiles, int n_tiles, int c, const float* halo,
-                            void* out, hipStream_t stream);
+hipError_t launch_csa_fixup(int out_dt, const TileRec* tiles, const int64_t* cu_dev, int batch, int n_tiles, int c,
+                            const float* halo, void* out, hipStream_t stream);
 
 }  // namespace seqcomp

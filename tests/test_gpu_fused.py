@@ -290,6 +290,34 @@ def test_varlen_fp8_config_every_round_and_xcd(gpu_device):
         torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("mode,out_dtype", [("csa", "bf16"), ("csa", "fp8"), ("hca", "bf16")])
+def test_planned_and_looked_up_tiles_agree(gpu_device, mode, out_dtype):
+    """Batches of up to 64 sequences find their tiles from the offsets inside
+    the kernels; larger ones take the planner's table.  70 sequences in one
+    call (planner) give bit for bit the entries (and fp8 scales) of the same
+    sequences in two calls of 64 and 6 (looked up): ragged lengths, empty
+    and shorter-than-m sequences, tile-aligned ones."""
+    m = 4 if mode == "csa" else 128
+    rng = np.random.default_rng(70)
+    lengths = rng.integers(0, 1600 if mode == "csa" else 3000, size=70)
+    lengths[[3, 17]] = 0
+    lengths[[5, 40]] = m - 1
+    lengths[[8, 66]] = 512
+    case = synth.compressor_case(mode, lengths, 64, 32, m, seed=71, in_dtype="bf16", bias_std=0.3,
+                                 device=gpu_device)
+    b = case.biases
+    Ba, Bb = (b["Ba"], b["Bb"]) if mode == "csa" else (b["B"], None)
+    cu = np.asarray(case.cu_seqlens, dtype=np.int64)
+    whole = sc.compress_fused(mode, case.H, case.Wt_cat, Ba, Bb, m, cu, out_dtype)
+    parts = [sc.compress_fused(mode, case.H, case.Wt_cat, Ba, Bb, m, cu[:65], out_dtype),
+             sc.compress_fused(mode, case.H[cu[64]:], case.Wt_cat, Ba, Bb, m, cu[64:] - cu[64], out_dtype)]
+    assert torch.equal(whole[0], torch.cat([parts[0][0], parts[1][0]]))
+    if out_dtype == "fp8":
+        assert torch.equal(whole[1], torch.cat([parts[0][1], parts[1][1]]))
+    if out_dtype == "bf16":
+        assert row_rel_err(to64(whole[0]), _oracle_full(case)).max() <= BF16_OBSERVED
+
+
 @pytest.mark.parametrize("mode,out_dtype", [("csa", "f32"), ("csa", "fp8"), ("hca", "bf16"), ("hca", "fp8")])
 def test_sequence_results_independent_of_packing(gpu_device, mode, out_dtype):
     """No kernel communicates between workgroups (the CSA halo is merged by a
