@@ -122,6 +122,38 @@ def _time_calls(torch, calls, steps: int, warmup: int = 2):
     return float(np.median(t)), float(t.min()), float(t.mean())
 
 
+def _time_interleaved(torch, named, steps: int, warm_ms: float = 150.0):
+    """{name: (median, minimum, mean) ms of one call} for several candidate
+    paths, timed round-robin after a shared warm-up of at least `warm_ms` of
+    calls.  Under a sustained matrix-core load the clock settles over ~100 ms,
+    so a path timed first, alone, would be timed on a still-changing clock.
+    Each value is a callable or a list cycled through (rotating input sets);
+    candidate i starts its rotation i sets later, so no call reads the inputs
+    the call just before it read."""
+    names = list(named)
+    seqs = {n: (c if isinstance(c, (list, tuple)) else [c]) for n, c in named.items()}
+    call = lambda i, n, k: seqs[n][(k + i) % len(seqs[n])]()
+    t0 = time.perf_counter()
+    k = 0
+    while k < 2 or (time.perf_counter() - t0) * 1e3 < warm_ms:
+        for i, n in enumerate(names):
+            call(i, n, k)
+        torch.cuda.synchronize()
+        k += 1
+    ev = {n: _events(torch, 2 * steps) for n in names}
+    for k in range(steps):
+        for i, n in enumerate(names):
+            ev[n][2 * k].record()
+            call(i, n, k)
+            ev[n][2 * k + 1].record()
+    torch.cuda.synchronize()
+    out = {}
+    for n in names:
+        t = np.array([ev[n][2 * k].elapsed_time(ev[n][2 * k + 1]) for k in range(steps)])
+        out[n] = (float(np.median(t)), float(t.min()), float(t.mean()))
+    return out
+
+
 def device_record(torch, dev):
     """The device's properties and a measured plain device-to-device copy of
     1 GiB (torch copy: 1 GiB read + 1 GiB written), beside the published
@@ -230,10 +262,8 @@ def csa_full_leg(sc, synth, torch, steps, cpu: bool):
     Wdn = case.Wt_cat.t().contiguous()
     Yr = torch.empty((T, 4 * c), dtype=torch.bfloat16, device=dev)
     blas = [lambda H=H: torch.mm(H, Wdn, out=Yr) for H in Hs]
-    med, mn, mean = _time_calls(torch, fused, steps)
-    pmed, pmn, _ = _time_calls(torch, proj, steps)
-    umed, umn, _ = _time_calls(torch, unfused, steps)
-    bmed, bmn, _ = _time_calls(torch, blas, steps)
+    r = _time_interleaved(torch, {"fused": fused, "proj": proj, "unfused": unfused, "blas": blas}, steps)
+    (med, mn, mean), (pmed, pmn, _), (umed, umn, _), (bmed, bmn, _) = r["fused"], r["proj"], r["unfused"], r["blas"]
     flops = 2.0 * T * d * 4 * c
     E = T // m
     res = {"workload": f"csa_full: one sequence, n={T}, d={d}, c={c}, m={m} -> {E} entries, bf16 in/out "
@@ -283,10 +313,8 @@ def hca_full_leg(sc, synth, torch, steps, cpu: bool):
     Wdn = case.Wt_cat.t().contiguous()
     Yr = torch.empty((T, 2 * c), dtype=torch.bfloat16, device=dev)
     blas = lambda: torch.mm(case.H, Wdn, out=Yr)
-    med, mn, _ = _time_calls(torch, fused, steps)
-    pmed, pmn, _ = _time_calls(torch, proj, steps)
-    umed, umn, _ = _time_calls(torch, unfused, steps)
-    bmed, bmn, _ = _time_calls(torch, blas, steps)
+    r = _time_interleaved(torch, {"fused": fused, "proj": proj, "unfused": unfused, "blas": blas}, steps)
+    (med, mn, _), (pmed, pmn, _), (umed, umn, _), (bmed, bmn, _) = r["fused"], r["proj"], r["unfused"], r["blas"]
     flops = 2.0 * T * d * 2 * c
     E = T // m
     res = {"workload": f"hca_full: one sequence, n={T}, d={d}, c={c}, m'={m} -> {E} entries, bf16 in/out",
@@ -635,7 +663,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--warmup", type=int, default=5,
+                    help="untimed steps first: the clock settles over ~100 ms of sustained matrix-core load")
     ap.add_argument("--pool-steps", type=int, default=20)
     ap.add_argument("--cpu-sample-tokens", type=int, default=262144)
     ap.add_argument("--cpu-one-core-tokens", type=int, default=16384)
