@@ -122,34 +122,32 @@ def _time_calls(torch, calls, steps: int, warmup: int = 2):
     return float(np.median(t)), float(t.min()), float(t.mean())
 
 
-def _time_interleaved(torch, named, steps: int, warm_ms: float = 150.0):
+def _time_settled(torch, named, steps: int, warm_ms: float = 150.0):
     """{name: (median, minimum, mean) ms of one call} for several candidate
-    paths, timed round-robin after a shared warm-up of at least `warm_ms` of
-    calls.  Under a sustained matrix-core load the clock settles over ~100 ms,
-    so a path timed first, alone, would be timed on a still-changing clock.
-    Each value is a callable or a list cycled through (rotating input sets);
-    candidate i starts its rotation i sets later, so no call reads the inputs
-    the call just before it read."""
-    names = list(named)
-    seqs = {n: (c if isinstance(c, (list, tuple)) else [c]) for n, c in named.items()}
-    call = lambda i, n, k: seqs[n][(k + i) % len(seqs[n])]()
-    t0 = time.perf_counter()
-    k = 0
-    while k < 2 or (time.perf_counter() - t0) * 1e3 < warm_ms:
-        for i, n in enumerate(names):
-            call(i, n, k)
-        torch.cuda.synchronize()
-        k += 1
-    ev = {n: _events(torch, 2 * steps) for n in names}
-    for k in range(steps):
-        for i, n in enumerate(names):
-            ev[n][2 * k].record()
-            call(i, n, k)
-            ev[n][2 * k + 1].record()
-    torch.cuda.synchronize()
+    paths, each timed in its steady state: it first runs alone for at least
+    `warm_ms` (under a sustained matrix-core load the clock settles over
+    ~100 ms, and settles differently after different work, so a path timed
+    right after a short warm-up, or after another path, would be timed on a
+    clock set by something else), then `steps` consecutive calls are timed.
+    Each value is a callable or a list cycled through (rotating input sets)."""
     out = {}
-    for n in names:
-        t = np.array([ev[n][2 * k].elapsed_time(ev[n][2 * k + 1]) for k in range(steps)])
+    for n, c in named.items():
+        seq = c if isinstance(c, (list, tuple)) else [c]
+        t0 = time.perf_counter()
+        k = 0
+        while k < 2 or (time.perf_counter() - t0) * 1e3 < warm_ms:
+            seq[k % len(seq)]()
+            k += 1
+            if k % 16 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        ev = _events(torch, 2 * steps)
+        for j in range(steps):
+            ev[2 * j].record()
+            seq[(k + j) % len(seq)]()
+            ev[2 * j + 1].record()
+        torch.cuda.synchronize()
+        t = np.array([ev[2 * j].elapsed_time(ev[2 * j + 1]) for j in range(steps)])
         out[n] = (float(np.median(t)), float(t.min()), float(t.mean()))
     return out
 
@@ -262,7 +260,7 @@ def csa_full_leg(sc, synth, torch, steps, cpu: bool):
     Wdn = case.Wt_cat.t().contiguous()
     Yr = torch.empty((T, 4 * c), dtype=torch.bfloat16, device=dev)
     blas = [lambda H=H: torch.mm(H, Wdn, out=Yr) for H in Hs]
-    r = _time_interleaved(torch, {"fused": fused, "proj": proj, "unfused": unfused, "blas": blas}, steps)
+    r = _time_settled(torch, {"fused": fused, "proj": proj, "unfused": unfused, "blas": blas}, steps)
     (med, mn, mean), (pmed, pmn, _), (umed, umn, _), (bmed, bmn, _) = r["fused"], r["proj"], r["unfused"], r["blas"]
     flops = 2.0 * T * d * 4 * c
     E = T // m
@@ -313,7 +311,7 @@ def hca_full_leg(sc, synth, torch, steps, cpu: bool):
     Wdn = case.Wt_cat.t().contiguous()
     Yr = torch.empty((T, 2 * c), dtype=torch.bfloat16, device=dev)
     blas = lambda: torch.mm(case.H, Wdn, out=Yr)
-    r = _time_interleaved(torch, {"fused": fused, "proj": proj, "unfused": unfused, "blas": blas}, steps)
+    r = _time_settled(torch, {"fused": fused, "proj": proj, "unfused": unfused, "blas": blas}, steps)
     (med, mn, _), (pmed, pmn, _), (umed, umn, _), (bmed, bmn, _) = r["fused"], r["proj"], r["unfused"], r["blas"]
     flops = 2.0 * T * d * 2 * c
     E = T // m
