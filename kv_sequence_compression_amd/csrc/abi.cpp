@@ -514,10 +514,15 @@ int seqcomp_rope_store(const void* entries, int in_dtype, int64_t c, int64_t m, 
   hipStream_t s = static_cast<hipStream_t>(stream);
   TileRec* tiles = static_cast<TileRec*>(workspace);
   const int n_tiles = (int)count_tiles(cu_seqlens_host, batch, m, m * kRopeTileEntries);
-  hipError_t e = launch_plan(cu_seqlens_dev, (int)batch, (int)m, (int)(m * kRopeTileEntries), tiles, n_tiles, s);
+  // few sequences: each workgroup looks its one tile up from the offsets, no planner launch
+  const bool planned = batch > kTileLookupMaxBatch;
+  hipError_t e = planned
+                     ? launch_plan(cu_seqlens_dev, (int)batch, (int)m, (int)(m * kRopeTileEntries), tiles, n_tiles, s)
+                     : hipSuccess;
   if (e == hipSuccess)
-    e = launch_rope_store(in_dtype, entries, (int)c, (int)m, cu_seqlens_dev, pos0_dev, (int)rope_dims, rope_base,
-                          slots_dev, n_slots, tiles, n_tiles, cache_nope, cache_scale, cache_rope, s);
+    e = launch_rope_store(in_dtype, entries, (int)c, (int)m, cu_seqlens_dev, (int)batch, pos0_dev, (int)rope_dims,
+                          rope_base, slots_dev, n_slots, planned ? tiles : nullptr, n_tiles, cache_nope, cache_scale,
+                          cache_rope, s);
   return hip_status(e);
 }
 

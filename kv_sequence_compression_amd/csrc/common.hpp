@@ -37,7 +37,7 @@ __device__ __forceinline__ TileRec tile_lookup(const int64_t* __restrict__ cu, i
     row0 = (int)start;
     ne = (int)((cu[lane + 1] - start) / m);
   }
-  const int nt = (ne * m + tile_rows - 1) / tile_rows;
+  const int nt = (int)(((int64_t)ne * m + tile_rows - 1) / tile_rows);
   int tend = nt, eend = ne;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {

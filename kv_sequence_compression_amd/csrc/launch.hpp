@@ -79,9 +79,10 @@ hipError_t launch_csa_append(int in_dt, int out_dt, const void* H, int64_t nb, i
 size_t append_partial_bytes(int64_t nb, int c);
 
 // Partial RoPE + mixed store of packed entries [E x c] (tiles of 64 entries
-// from the planner with tile_rows = 64 m).
+// with tile_rows = 64 m: the planner's table, or NULL for batches of at most
+// kTileLookupMaxBatch sequences, whose workgroups look their tiles up).
 constexpr int kRopeTileEntries = 64;
-hipError_t launch_rope_store(int in_dt, const void* entries, int c, int m, const int64_t* cu_dev,
+hipError_t launch_rope_store(int in_dt, const void* entries, int c, int m, const int64_t* cu_dev, int batch,
                              const int64_t* pos0_dev, int r, double rope_base, const int64_t* slots_dev,
                              int64_t n_slots, const TileRec* tiles, int n_tiles, uint8_t* nope, float* scale,
                              uint16_t* rope, hipStream_t stream);

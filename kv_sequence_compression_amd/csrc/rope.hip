@@ -83,14 +83,17 @@ __device__ __forceinline__ void load8_stream(const char* p, float (&x)[8]) {
   }
 }
 
-template <int DIN>
+// LOOKUP: the workgroup finds its tile from the sequence offsets (tile_lookup,
+// at most kTileLookupMaxBatch sequences) instead of the planner's table; a
+// separate instantiation, so the kernel that reads the table is unchanged.
+template <int DIN, bool LOOKUP = false>
 __global__ __launch_bounds__(kRopeThreads) void rope_store_kernel(
     const char* __restrict__ entries, int c, int m, const int64_t* __restrict__ cu, const int64_t* __restrict__ pos0,
     int r, double log2_base, const int64_t* __restrict__ slots, int64_t n_slots, const TileRec* __restrict__ tiles,
-    uint8_t* __restrict__ nope, float* __restrict__ scale, uint16_t* __restrict__ rope) {
+    uint8_t* __restrict__ nope, float* __restrict__ scale, uint16_t* __restrict__ rope, int batch) {
   constexpr int ES = DTypeSize<DIN>::value;
   constexpr int G = 4;
-  const TileRec t = tiles[blockIdx.x];
+  const TileRec t = LOOKUP ? tile_lookup(cu, batch, m, m * kRopeTileEntries, blockIdx.x) : tiles[blockIdx.x];
   const int seq = tile_seq(t.flags);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int ne = t.n_rows / m;
@@ -181,19 +184,17 @@ __global__ __launch_bounds__(kRopeThreads) void rope_store_kernel(
 
 }  // namespace
 
-hipError_t launch_rope_store(int in_dt, const void* entries, int c, int m, const int64_t* cu_dev,
+hipError_t launch_rope_store(int in_dt, const void* entries, int c, int m, const int64_t* cu_dev, int batch,
                              const int64_t* pos0_dev, int r, double rope_base, const int64_t* slots_dev,
                              int64_t n_slots, const TileRec* tiles, int n_tiles, uint8_t* nope, float* scale,
                              uint16_t* rope, hipStream_t stream) {
   const double lb = log2(rope_base);
-  if (in_dt == DT_BF16)
-    hipLaunchKernelGGL(rope_store_kernel<DT_BF16>, dim3(n_tiles), dim3(kRopeThreads), 0, stream,
-                       static_cast<const char*>(entries), c, m, cu_dev, pos0_dev, r, lb, slots_dev, n_slots, tiles,
-                       nope, scale, rope);
-  else
-    hipLaunchKernelGGL(rope_store_kernel<DT_F32>, dim3(n_tiles), dim3(kRopeThreads), 0, stream,
-                       static_cast<const char*>(entries), c, m, cu_dev, pos0_dev, r, lb, slots_dev, n_slots, tiles,
-                       nope, scale, rope);
+  auto args = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(n_tiles), dim3(kRopeThreads), 0, stream, static_cast<const char*>(entries), c, m,
+                       cu_dev, pos0_dev, r, lb, slots_dev, n_slots, tiles, nope, scale, rope, batch);
+  };
+  if (in_dt == DT_BF16) tiles ? args(rope_store_kernel<DT_BF16>) : args(rope_store_kernel<DT_BF16, true>);
+  else tiles ? args(rope_store_kernel<DT_F32>) : args(rope_store_kernel<DT_F32, true>);
   return hipGetLastError();
 }
 

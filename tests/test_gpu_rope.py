@@ -98,6 +98,25 @@ def test_fused_then_store_matches_oracle(gpu_device):
     assert np.max(np.abs(to64(out) - ref)) <= 2e-5
 
 
+def test_rope_store_many_sequences(gpu_device):
+    """70 sequences (past the 64 whose tiles the kernel looks up itself: the
+    planner's table), ragged lengths with empty and short ones, random
+    offsets: against the oracle store."""
+    rng = np.random.default_rng(14)
+    lengths = rng.integers(0, 700, size=70)
+    lengths[[2, 30]] = 0
+    lengths[[7, 50]] = 3
+    cu = synth.cu_from_lengths(lengths)
+    m, c, r = 4, 256, 64
+    E = int(sum(L // m for L in lengths))
+    X = synth.normal((E, c), 1.0, (14, 1), "cpu", "f32").double().numpy()
+    pos0 = rng.integers(0, 100000, size=70)
+    cache = sc.rope_cache(E, c, r, gpu_device)
+    sc.rope_store(torch.from_numpy(X).float().to(gpu_device), m, cu, cache, r, pos0=pos0)
+    torch.cuda.synchronize()
+    _check(cache, np.arange(E), X, oracle.entry_positions(cu, m, pos0), r)
+
+
 def test_rope_store_wide_entries(gpu_device):
     """c > 512 takes the chunked path: 1024 channels, 128 of them rotated."""
     lengths = [4 * 9, 4 * 70]
