@@ -266,6 +266,7 @@ def csa_full_leg(sc, synth, torch, steps, cpu: bool):
     E = T // m
     res = {"workload": f"csa_full: one sequence, n={T}, d={d}, c={c}, m={m} -> {E} entries, bf16 in/out "
                        "(3 rotating hidden-state sets)",
+           "timing": f"each path alone for >= 150 ms, then {steps} consecutive calls timed with HIP events",
            "ms_median": med, "ms_min": mn, "entries_per_s": E / (med * 1e-3), "tokens_per_s": T / (med * 1e-3),
            "roofline": _mfma_roofline(flops, med, "fused CSA call (planner + tile kernel + halo fix-up)",
                                       "fused_csa_full"),
@@ -316,6 +317,7 @@ def hca_full_leg(sc, synth, torch, steps, cpu: bool):
     flops = 2.0 * T * d * 2 * c
     E = T // m
     res = {"workload": f"hca_full: one sequence, n={T}, d={d}, c={c}, m'={m} -> {E} entries, bf16 in/out",
+           "timing": f"each path alone for >= 150 ms, then {steps} consecutive calls timed with HIP events",
            "ms_median": med, "ms_min": mn, "entries_per_s": E / (med * 1e-3), "tokens_per_s": T / (med * 1e-3),
            "roofline": _mfma_roofline(flops, med, "fused HCA call (planner + tile kernel)", "fused_hca_full"),
            "project_alone": {"ms_median": pmed, "ms_min": pmn,
